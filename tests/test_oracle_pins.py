@@ -1,0 +1,343 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these tests retypes the oracle's formulas: each compares the oracle with an
+independent route -- hand-worked exact values, a library integer matmul on inputs
+where the method reduces to it, exhaustive enumeration, a bit-plane popcount
+re-derivation, closed forms, exact invariants and a Gaussian statistic -- chosen so
+that a plausible slip (threshold gamma instead of gamma/2, half-away rounding, a
+dropped term, a transposed operand, a wrong sign, a missing scale) fails at least one.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_ternary_weight_absmean_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+
+def _hex32(s):
+    return np.float32(float.fromhex(s))
+
+
+def tol_ok(y, ref):
+    """|y - ref| <= 1e-5 |ref| + 1e-6, the output tolerance of the method's contract."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return np.all(np.abs(y - ref) <= 1e-5 * np.abs(ref) + 1e-6)
+
+
+# ---------------------------------------------------------------- hand examples
+with open(GOLDEN) as f:
+    _EXAMPLES = json.load(f)["examples"]
+
+
+@pytest.mark.parametrize("ex", _EXAMPLES, ids=[e["name"] for e in _EXAMPLES])
+def test_hand_examples(orc, ex):
+    W = np.array(ex["W"], dtype=np.float32)
+    X = np.array(ex["X"], dtype=np.float32)
+    r = oracle.linear(W, X, orc)
+    assert r["gamma"] == _hex32(ex["gamma"])
+    np.testing.assert_array_equal(r["T"], np.array(ex["T"], dtype=np.int8))
+    np.testing.assert_array_equal(r["Q"], np.array(ex["Q"], dtype=np.int8))
+    np.testing.assert_array_equal(r["s_x"], np.array([_hex32(s) for s in ex["s_x"]], dtype=np.float32))
+    np.testing.assert_array_equal(r["qsum"], np.array(ex["qsum"], dtype=np.int32))
+    np.testing.assert_array_equal(r["acc"], np.array(ex["acc"], dtype=np.int32))
+    Yref = np.array([[_hex32(s) for s in row] for row in ex["Y"]], dtype=np.float32)
+    if ex["Y_exact"]:
+        np.testing.assert_array_equal(r["Y"], Yref)
+    else:
+        assert tol_ok(r["Y"], Yref)
+
+
+# ------------------------------------------------- reduction to integer matmul
+def _int_acts(rng, M, K):
+    """Integer-valued activations whose row absmax is exactly 127: quantization is the identity."""
+    X = rng.integers(-127, 128, size=(M, K)).astype(np.float32)
+    cols = rng.integers(0, K, size=M)
+    X[np.arange(M), cols] = rng.choice([-127.0, 127.0], size=M)
+    return X
+
+
+def test_ternary_times_integer_is_library_matmul(orc):
+    """W = c*T and integer X with absmax 127 reduce the method to an integer matmul."""
+    rng = np.random.default_rng(11)
+    M, N, K = 7, 37, 129
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    c = np.float32(0.375)
+    W = c * T.astype(np.float32)
+    X = _int_acts(rng, M, K)
+    r = oracle.linear(W, X, orc)
+    np.testing.assert_array_equal(r["T"], T)
+    np.testing.assert_array_equal(r["Q"], X.astype(np.int8))
+    np.testing.assert_array_equal(r["s_x"], np.ones(M, np.float32))
+    ref = X.astype(np.int64) @ T.astype(np.int64).T
+    np.testing.assert_array_equal(r["acc"], ref.astype(np.int32))
+    # gamma = c * nnz / (N K) exactly
+    g = Fraction(float(c)) * int(np.count_nonzero(T)) / (N * K)
+    assert r["gamma"] == np.float32(float(g)) or abs(float(r["gamma"]) - float(g)) <= 2**-24 * float(g)
+
+
+def test_brute_force_all_2x3_ternary(orc):
+    """Every one of the 3^6 ternary 2x3 matrices, times random integer activations."""
+    rng = np.random.default_rng(5)
+    X = _int_acts(rng, 4, 3)
+    Xi = X.astype(np.int64)
+    for idx in range(3 ** 6):
+        digits = [(idx // 3 ** i) % 3 - 1 for i in range(6)]
+        T = np.array(digits, dtype=np.int8).reshape(2, 3)
+        W = np.float32(0.5) * T.astype(np.float32)
+        r = oracle.linear(W, X, orc)
+        np.testing.assert_array_equal(r["T"], T)
+        expect = Xi @ T.astype(np.int64).T
+        np.testing.assert_array_equal(r["acc"], expect)
+        # y = acc * gamma * 1 exactly representable here -> within tolerance of the fp64 product
+        assert tol_ok(r["Y"], expect * np.float64(r["gamma"]))
+
+
+def test_brute_force_1x4_rows_against_pm127_grid(orc):
+    """All 81 ternary 1x4 rows against every activation row over {-127,-1,0,1,127}^4 with absmax 127."""
+    vals = np.array([-127, -1, 0, 1, 127], dtype=np.float32)
+    grid = np.array(np.meshgrid(vals, vals, vals, vals, indexing="ij")).reshape(4, -1).T
+    X = grid[np.max(np.abs(grid), axis=1) == 127]
+    T = np.array(np.meshgrid(*([np.array([-1, 0, 1])] * 4), indexing="ij")).reshape(4, -1).T.astype(np.int8)
+    Q, s, qs = oracle.quant_act(X, orc)
+    np.testing.assert_array_equal(Q, X.astype(np.int8))
+    acc = oracle.ternary_matmul(T, Q, orc)
+    expect = np.einsum("mk,nk->mn", X.astype(np.int64), T.astype(np.int64))
+    np.testing.assert_array_equal(acc, expect)
+
+
+# ------------------------------------------------- independent integer routes
+def test_add_subtract_skip_form(orc):
+    """acc = sum of q where t = +1 minus sum of q where t = -1 ("BitCompute" page, "Features")."""
+    rng = np.random.default_rng(3)
+    M, N, K = 5, 23, 301
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    Q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    acc = oracle.ternary_matmul(T, Q, orc)
+    for m in range(M):
+        for n in range(N):
+            plus = int(Q[m][T[n] == 1].astype(np.int64).sum())
+            minus = int(Q[m][T[n] == -1].astype(np.int64).sum())
+            assert acc[m, n] == plus - minus
+
+
+def test_bitplane_popcount_form(orc):
+    """Bit-plane identity after the "bit-floor" page, "The core math", widened to int8 activations.
+
+    t is split into a magnitude plane (t != 0) and a sign plane (t < 0); q is split into its
+    two's-complement bit-planes q_b with weights 2^b (b < 7) and -128 (b = 7). Then
+    acc = sum_b w_b * (popcount(pos & q_b) - popcount(neg & q_b)), pos = mag & ~sign,
+    neg = mag & sign -- integer popcounts only, no multiplies.
+    """
+    rng = np.random.default_rng(4)
+    M, N, K = 3, 11, 200
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    Q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    acc = oracle.ternary_matmul(T, Q, orc)
+    mag = T != 0
+    sign = T < 0
+    pos = mag & ~sign
+    neg = mag & sign
+    qu = Q.view(np.uint8)
+    for m in range(M):
+        for n in range(N):
+            total = 0
+            for b in range(8):
+                plane = ((qu[m] >> b) & 1).astype(bool)
+                wb = -128 if b == 7 else (1 << b)
+                total += wb * (int(np.count_nonzero(pos[n] & plane)) - int(np.count_nonzero(neg[n] & plane)))
+            assert acc[m, n] == total
+
+
+# ------------------------------------------------------------- the weight scale
+def test_gamma_is_exact_mean_rounded(orc):
+    """gamma equals fp32(exact mean |W|) (math.fsum is exact) on random and ragged shapes."""
+    for seed, (N, K) in enumerate([(1, 1), (3, 5), (17, 300), (64, 257), (130, 1000)]):
+        W = synth.gaussian((N, K), 100 + seed, 0.02)
+        g = oracle.absmean(W, orc)
+        exact = Fraction(math.fsum(np.abs(W.astype(np.float64)).ravel().tolist())) / (N * K)
+        ref = np.float32(float(exact))  # float(Fraction) is correctly rounded; fp64->fp32 tie-free here
+        assert abs(float(g) - float(ref)) <= np.spacing(ref), (N, K, g, ref)
+
+
+def test_gamma_scale_and_sign_exact(orc):
+    rng = np.random.default_rng(9)
+    W = synth.gaussian((40, 96), 7, 0.02)
+    g = oracle.absmean(W, orc)
+    assert oracle.absmean(-W, orc) == g
+    assert oracle.absmean(np.float32(8.0) * W, orc) == np.float32(8.0) * g
+    assert oracle.absmean(W[rng.permutation(40)], orc) == pytest.approx(float(g), rel=1e-7)
+
+
+def test_gamma_gaussian_statistic(orc):
+    """For W ~ N(0, s^2), mean|W| -> s*sqrt(2/pi)."""
+    W, _ = synth.tiny_matmul()
+    g = float(oracle.absmean(W, orc))
+    expect = 0.02 * math.sqrt(2 / math.pi)
+    # standard error of the mean of |z| over 131072 draws is ~0.6/362 of s; 5 sigma
+    assert abs(g - expect) < 5 * 0.02 * math.sqrt(1 - 2 / math.pi) / math.sqrt(W.size)
+
+
+def test_zero_fraction_gaussian(orc):
+    """Zero fraction -> P(|z| <= sqrt(2/pi)/2) = erf(1/sqrt(4*pi)) = 0.3101 (threshold gamma/2).
+
+    A threshold at gamma would give 0.575; the 7B decode workload's "~1/3 zeros" is this number.
+    """
+    W, _ = synth.tiny_matmul()
+    g = oracle.absmean(W, orc)
+    T = oracle.ternarize(W, g, orc)
+    p0 = math.erf(math.sqrt(2 / math.pi) / 2 / math.sqrt(2))
+    assert abs(p0 - 0.3101) < 1e-3
+    frac0 = float(np.mean(T == 0))
+    assert abs(frac0 - p0) < 0.01
+    assert abs(float(np.mean(T == 1)) - (1 - p0) / 2) < 0.01
+    assert abs(float(np.mean(T == -1)) - (1 - p0) / 2) < 0.01
+
+
+def test_ternary_idempotent(orc):
+    """W = c*T (c > 0) ternarizes back to exactly T, since gamma/2 <= c/2 < c."""
+    rng = np.random.default_rng(21)
+    for c in (np.float32(1e-3), np.float32(0.02), np.float32(3.0)):
+        T = rng.integers(-1, 2, size=(31, 77)).astype(np.int8)
+        W = c * T.astype(np.float32)
+        g = oracle.absmean(W, orc)
+        np.testing.assert_array_equal(oracle.ternarize(W, g, orc), T)
+
+
+# --------------------------------------------------------- activation quantizer
+def test_quant_rounding_bound_and_range(orc):
+    """|x - q*s_x| <= s_x/2 (+ fp32 slack), |q| <= 127 and each row's absmax maps to +-127."""
+    X = synth.gaussian((50, 333), 77)
+    Q, s, qs = oracle.quant_act(X, orc)
+    a = np.max(np.abs(X), axis=1)
+    assert np.all(np.abs(Q.astype(np.int32)) <= 127)
+    np.testing.assert_array_equal(np.max(np.abs(Q.astype(np.int32)), axis=1), 127)
+    err = np.abs(X.astype(np.float64) - Q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None] * (0.5 + 1e-5))
+    np.testing.assert_array_equal(qs, Q.astype(np.int32).sum(axis=1))
+    # s_x is the fp32 a/127 (within 1 ulp of the exact ratio)
+    assert np.all(np.abs(s.astype(np.float64) - a.astype(np.float64) / 127) <= np.spacing(s))
+
+
+def test_quant_odd_and_scale_invariant(orc):
+    X = synth.gaussian((9, 130), 78)
+    Q, s, qs = oracle.quant_act(X, orc)
+    Qn, sn, qsn = oracle.quant_act(-X, orc)
+    np.testing.assert_array_equal(Qn, -Q)
+    np.testing.assert_array_equal(sn, s)
+    np.testing.assert_array_equal(qsn, -qs)
+    for j in (-3, 5):
+        Qj, sj, _ = oracle.quant_act(np.float32(2.0 ** j) * X, orc)
+        np.testing.assert_array_equal(Qj, Q)
+        np.testing.assert_array_equal(sj, np.float32(2.0 ** j) * s)
+
+
+def test_quant_zero_row(orc):
+    X = synth.gaussian((3, 40), 79)
+    X[1] = 0.0
+    Q, s, qs = oracle.quant_act(X, orc)
+    assert not Q[1].any() and s[1] == 0 and qs[1] == 0
+    assert s[0] > 0 and s[2] > 0
+
+
+# ----------------------------------------------------------- layer invariants
+def _layer(orc, seed, M=6, N=33, K=250):
+    W = synth.gaussian((N, K), seed, 0.02)
+    X = synth.gaussian((M, K), seed + 1)
+    return W, X, oracle.linear(W, X, orc)
+
+
+def test_zero_weights_give_zero(orc):
+    X = synth.gaussian((4, 64), 80)
+    r = oracle.linear(np.zeros((8, 64), np.float32), X, orc)
+    assert r["gamma"] == 0 and not r["T"].any() and not r["acc"].any()
+    assert np.all(r["Y"] == 0)
+
+
+def test_negating_w_negates_y(orc):
+    W, X, r = _layer(orc, 200)
+    rn = oracle.linear(-W, X, orc)
+    np.testing.assert_array_equal(rn["T"], -r["T"])
+    np.testing.assert_array_equal(rn["acc"], -r["acc"])
+    np.testing.assert_array_equal(rn["Y"], -r["Y"])
+
+
+def test_negating_x_negates_acc(orc):
+    W, X, r = _layer(orc, 210)
+    rn = oracle.linear(W, -X, orc)
+    np.testing.assert_array_equal(rn["acc"], -r["acc"])
+    np.testing.assert_array_equal(rn["Y"], -r["Y"])
+
+
+def test_power_of_two_scaling(orc):
+    W, X, r = _layer(orc, 220)
+    r2 = oracle.linear(np.float32(4.0) * W, np.float32(0.5) * X, orc)
+    np.testing.assert_array_equal(r2["T"], r["T"])
+    np.testing.assert_array_equal(r2["acc"], r["acc"])
+    np.testing.assert_array_equal(r2["Y"], np.float32(2.0) * r["Y"])
+
+
+def test_row_permutation_permutes_acc(orc):
+    W, X, r = _layer(orc, 230)
+    perm = np.random.default_rng(1).permutation(W.shape[0])
+    acc_p = oracle.ternary_matmul(r["T"][perm], r["Q"], orc)
+    np.testing.assert_array_equal(acc_p, r["acc"][:, perm])
+
+
+def test_acc_bound(orc):
+    W, X, r = _layer(orc, 240)
+    nnz = np.count_nonzero(r["T"], axis=1)
+    assert np.all(np.abs(r["acc"]) <= 127 * nnz[None, :])
+
+
+def test_y_equals_matmul_of_dequantized_operands(orc):
+    """y equals the plain matmul of the dequantized operands (q*s_x)(t*gamma)^T within tolerance.
+
+    The "BitCompute" page, "Benchmark Analysis", describes the same product as the fake-quantized
+    simulation; fp64 keeps the K-term summation error far below the tolerance.
+    """
+    for seed, (M, N, K) in enumerate([(1, 64, 256), (16, 50, 700), (128, 512, 256)]):
+        W, X, r = _layer(orc, 300 + 10 * seed, M, N, K)
+        deq_x = r["Q"].astype(np.float64) * r["s_x"].astype(np.float64)[:, None]
+        deq_w = r["T"].astype(np.float64) * np.float64(r["gamma"])
+        assert tol_ok(r["Y"], deq_x @ deq_w.T)
+
+
+def test_tiny_workload_pipeline(orc):
+    """The tiny matmul workload (X [128,256], W [512,256]) runs end to end with sane statistics."""
+    W, X = synth.tiny_matmul()
+    r = oracle.linear(W, X, orc)
+    assert r["Y"].shape == (128, 512) and r["acc"].dtype == np.int32
+    assert np.all(r["s_x"] > 0)
+    deq = (r["Q"].astype(np.float64) * r["s_x"][:, None]) @ (r["T"].astype(np.float64) * float(r["gamma"])).T
+    assert tol_ok(r["Y"], deq)
+
+
+# ----------------------------------------------------------------- edge cases
+def test_empty_shapes(orc):
+    assert oracle.absmean(np.zeros((0, 5), np.float32), orc) == 0
+    assert oracle.absmean(np.zeros((5, 0), np.float32), orc) == 0
+    Q, s, qs = oracle.quant_act(np.zeros((0, 7), np.float32), orc)
+    assert Q.shape == (0, 7) and s.shape == (0,)
+    Q, s, qs = oracle.quant_act(np.zeros((3, 0), np.float32), orc)
+    assert np.all(s == 0) and np.all(qs == 0)
+    acc = oracle.ternary_matmul(np.zeros((4, 0), np.int8), np.zeros((3, 0), np.int8), orc)
+    assert acc.shape == (3, 4) and not acc.any()
+
+
+def test_nonfinite_rejected(orc):
+    W = np.ones((2, 3), np.float32)
+    W[1, 2] = np.nan
+    with pytest.raises(oracle.OracleInputError):
+        oracle.absmean(W, orc)
+    X = np.ones((2, 3), np.float32)
+    X[0, 0] = np.inf
+    with pytest.raises(oracle.OracleInputError):
+        oracle.quant_act(X, orc)
