@@ -1,1 +1,33 @@
-"""MI355X-native BitNet b1.58 W1.58A8 ternary linear layer (placeholder during bring-up)."""
+"""MI355X-native BitNet b1.58 W1.58A8 ternary linear layer.
+
+The compute lives in ``libbt.so`` (hand-written HIP kernels for gfx950 behind the C ABI
+of ``include/bt.h``). This module only marshals torch tensors (device memory) and the
+current HIP stream into those calls; every step of the path runs in the library's
+kernels. Names follow the C ABI: ``pack_weights``, ``quant_act``, ``ternary_gemv``,
+``ternary_gemm`` (+ ``unpack_weights``, ``linear``).
+"""
+from __future__ import annotations
+
+from ._lib import BTError, lib
+from .api import (
+    GEMV_AUTO,
+    GEMV_DOT4,
+    GEMV_MAX_M,
+    GEMV_MFMA,
+    PackedWeight,
+    act_row_bytes,
+    linear,
+    pack_weights,
+    pack_workspace_bytes,
+    packed_weight_bytes,
+    quant_act,
+    ternary_gemm,
+    ternary_gemv,
+    unpack_weights,
+)
+
+__all__ = [
+    "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_MFMA", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
+    "linear", "pack_weights", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
+    "ternary_gemv", "unpack_weights",
+]

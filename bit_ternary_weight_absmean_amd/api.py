@@ -1,0 +1,129 @@
+"""Torch-facing wrappers over the C ABI (argument marshalling only).
+
+Every function takes and returns torch tensors on a HIP device, passes raw device
+pointers and ``torch.cuda.current_stream().cuda_stream`` to libbt.so, and checks the
+returned status. Nothing here computes any part of the method.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from ._lib import check, lib
+
+GEMV_AUTO, GEMV_DOT4, GEMV_MFMA = 0, 1, 2
+GEMV_MAX_M = 16
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def packed_weight_bytes(N: int, K: int) -> int:
+    return int(lib().bt_packed_weight_bytes(N, K))
+
+
+def act_row_bytes(K: int) -> int:
+    return int(lib().bt_act_row_bytes(K))
+
+
+def pack_workspace_bytes(N: int, K: int) -> int:
+    return int(lib().bt_pack_workspace_bytes(N, K))
+
+
+@dataclass
+class PackedWeight:
+    """A 2-bit packed ternary weight matrix and its absmean scale (both on device)."""
+
+    data: torch.Tensor   # uint8 [packed_weight_bytes(N, K)]
+    scale: torch.Tensor  # float32 [1], gamma
+    N: int
+    K: int
+
+
+def pack_weights(W: torch.Tensor, workspace: torch.Tensor | None = None) -> PackedWeight:
+    """bt_pack_weights: absmean ternarization + 2-bit packing of W [N,K] fp32."""
+    _need(W, "W", torch.float32)
+    N, K = W.shape
+    dev = W.device
+    data = torch.empty(max(packed_weight_bytes(N, K), 16), dtype=torch.uint8, device=dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    ws_bytes = pack_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError("workspace too small")
+    check(lib().bt_pack_weights(_ptr(W), N, K, _ptr(data), _ptr(scale), _ptr(workspace), _stream(dev)))
+    return PackedWeight(data, scale, N, K)
+
+
+def unpack_weights(pw: PackedWeight) -> torch.Tensor:
+    """bt_unpack_weights: the ternary codes t in {-1,0,1} as int8 [N,K]."""
+    T = torch.empty((pw.N, pw.K), dtype=torch.int8, device=pw.data.device)
+    check(lib().bt_unpack_weights(_ptr(pw.data), pw.N, pw.K, _ptr(T), _stream(pw.data.device)))
+    return T
+
+
+def quant_act(X: torch.Tensor, out=None):
+    """bt_quant_act: per-token absmax int8. Returns (Xq [M, act_row_bytes(K)] int8, s_x [M], x_sum [M])."""
+    _need(X, "X", torch.float32)
+    M, K = X.shape
+    dev = X.device
+    if out is None:
+        Xq = torch.empty((M, act_row_bytes(K)), dtype=torch.int8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+        xsum = torch.empty(M, dtype=torch.int32, device=dev)
+    else:
+        Xq, sx, xsum = out
+    check(lib().bt_quant_act(_ptr(X), M, K, _ptr(Xq), _ptr(sx), _ptr(xsum), _stream(dev)))
+    return Xq, sx, xsum
+
+
+def _product(fn_name, pw: PackedWeight, q, want_y, want_acc, out_y, out_acc, algo=None):
+    Xq, sx, xsum = q
+    M = sx.shape[0]
+    dev = pw.data.device
+    Y = out_y if out_y is not None else (
+        torch.empty((M, pw.N), dtype=torch.float32, device=dev) if want_y else None)
+    acc = out_acc if out_acc is not None else (
+        torch.empty((M, pw.N), dtype=torch.int32, device=dev) if want_acc else None)
+    args = [_ptr(pw.data), _ptr(pw.scale), _ptr(Xq), _ptr(sx), _ptr(xsum), M, pw.N, pw.K, _ptr(Y), _ptr(acc)]
+    if algo is not None:
+        args.append(algo)
+    check(getattr(lib(), fn_name)(*args, _stream(dev)))
+    return Y, acc
+
+
+def ternary_gemv(pw: PackedWeight, q, want_y=True, want_acc=False, out_y=None, out_acc=None, algo=GEMV_AUTO):
+    """bt_ternary_gemv_algo: decode product for M <= 16 tokens. Returns (Y, acc)."""
+    return _product("bt_ternary_gemv_algo", pw, q, want_y, want_acc, out_y, out_acc, algo)
+
+
+def ternary_gemm(pw: PackedWeight, q, want_y=True, want_acc=False, out_y=None, out_acc=None):
+    """bt_ternary_gemm: prefill product on int8 MFMA for any M. Returns (Y, acc)."""
+    return _product("bt_ternary_gemm", pw, q, want_y, want_acc, out_y, out_acc)
+
+
+def linear(X: torch.Tensor, pw: PackedWeight) -> torch.Tensor:
+    """Y = the W1.58A8 layer applied to X [M,K] fp32: quant_act then gemv (M <= 16) or gemm."""
+    q = quant_act(X)
+    M = X.shape[0]
+    if M <= GEMV_MAX_M:
+        Y, _ = ternary_gemv(pw, q)
+    else:
+        Y, _ = ternary_gemm(pw, q)
+    return Y

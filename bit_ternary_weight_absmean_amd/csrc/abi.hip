@@ -1,0 +1,211 @@
+// C ABI of libbt.so: argument validation, kernel selection and status codes.
+// Every check runs on the host before any HIP call, so a rejected call enqueues
+// nothing. The library allocates nothing and keeps no pointer past a call.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "bt.h"
+#include "bt_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+bt_status fail(bt_status code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bt_status ok()
+{
+    g_err[0] = '\0';
+    return BT_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bt_status hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(BT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bt_status check_k(int64_t K)
+{
+    if (K < 0 || K > BT_MAX_K)
+        return fail(BT_ERR_SHAPE, "K = %lld outside [0, %d]", (long long)K, BT_MAX_K);
+    return BT_OK;
+}
+
+// Common validation of the GEMV / GEMM arguments.
+bt_status check_product(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
+                        const int32_t *x_sum, int64_t M, int64_t N, int64_t K, const float *Y, const int32_t *acc)
+{
+    if (M < 0 || N < 0)
+        return fail(BT_ERR_SHAPE, "negative shape M = %lld, N = %lld", (long long)M, (long long)N);
+    if (bt_status s = check_k(K))
+        return s;
+    if (N > (int64_t)1 << 30 || M > (int64_t)1 << 30)
+        return fail(BT_ERR_SHAPE, "M = %lld or N = %lld above 2^30", (long long)M, (long long)N);
+    if (!Y && !acc)
+        return fail(BT_ERR_NULL, "Y and acc are both NULL");
+    if (M == 0 || N == 0)
+        return BT_OK;
+    // With K == 0 there are no weight or activation bytes: Wp and Xq may be NULL.
+    if (!w_scale || !x_scale || !x_sum || (K > 0 && (!Wp || !Xq)))
+        return fail(BT_ERR_NULL, "NULL input pointer");
+    if ((Wp && !aligned(Wp, 16)) || (Xq && !aligned(Xq, 16)))
+        return fail(BT_ERR_ALIGN, "Wp and Xq must be 16-byte aligned");
+    if (!aligned(w_scale, 4) || !aligned(x_scale, 4) || !aligned(x_sum, 4) || (Y && !aligned(Y, 4)) ||
+        (acc && !aligned(acc, 4)))
+        return fail(BT_ERR_ALIGN, "scale, sum and output arrays must be 4-byte aligned");
+    return BT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bt_packed_weight_bytes(int64_t N, int64_t K)
+{
+    if (N <= 0 || K <= 0)
+        return 0;
+    return (size_t)(bt::round_up(N, 64) * bt::round_up(K, 64) / 4);
+}
+
+int64_t bt_act_row_bytes(int64_t K) { return K <= 0 ? 0 : bt::round_up(K, 64); }
+
+size_t bt_pack_workspace_bytes(int64_t N, int64_t K)
+{
+    if (N <= 0 || K <= 0)
+        return 0;
+    return (size_t)bt::round_up(N * 8, 256);
+}
+
+bt_status bt_pack_weights(const float *W, int64_t N, int64_t K, void *Wp, float *w_scale, void *workspace,
+                          void *stream)
+{
+    if (N < 0 || N > (int64_t)1 << 30)
+        return fail(BT_ERR_SHAPE, "N = %lld outside [0, 2^30]", (long long)N);
+    if (bt_status s = check_k(K))
+        return s;
+    if (!w_scale)
+        return fail(BT_ERR_NULL, "w_scale is NULL");
+    if (!aligned(w_scale, 4))
+        return fail(BT_ERR_ALIGN, "w_scale must be 4-byte aligned");
+    const bool empty = (N == 0 || K == 0);
+    if (!empty) {
+        if (!W || !Wp || !workspace)
+            return fail(BT_ERR_NULL, "NULL W, Wp or workspace");
+        if (!aligned(W, 16) || !aligned(Wp, 16))
+            return fail(BT_ERR_ALIGN, "W and Wp must be 16-byte aligned");
+        if (!aligned(workspace, 8))
+            return fail(BT_ERR_ALIGN, "workspace must be 8-byte aligned");
+    }
+    return hip_status(bt::launch_pack(W, N, K, static_cast<uint4 *>(Wp), w_scale, static_cast<double *>(workspace),
+                                      static_cast<hipStream_t>(stream)),
+                      "bt_pack_weights launch");
+}
+
+bt_status bt_unpack_weights(const void *Wp, int64_t N, int64_t K, int8_t *T, void *stream)
+{
+    if (N < 0 || N > (int64_t)1 << 30)
+        return fail(BT_ERR_SHAPE, "N = %lld outside [0, 2^30]", (long long)N);
+    if (bt_status s = check_k(K))
+        return s;
+    if (N == 0 || K == 0)
+        return ok();
+    if (!Wp || !T)
+        return fail(BT_ERR_NULL, "NULL Wp or T");
+    if (!aligned(Wp, 16))
+        return fail(BT_ERR_ALIGN, "Wp must be 16-byte aligned");
+    return hip_status(bt::launch_unpack(static_cast<const uint4 *>(Wp), N, K, T, static_cast<hipStream_t>(stream)),
+                      "bt_unpack_weights launch");
+}
+
+bt_status bt_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale, int32_t *x_sum,
+                       void *stream)
+{
+    if (M < 0 || M > (int64_t)1 << 30)
+        return fail(BT_ERR_SHAPE, "M = %lld outside [0, 2^30]", (long long)M);
+    if (bt_status s = check_k(K))
+        return s;
+    if (M == 0)
+        return ok();
+    if (!x_scale || !x_sum || (K > 0 && (!X || !Xq)))
+        return fail(BT_ERR_NULL, "NULL X, Xq, x_scale or x_sum");
+    if ((X && !aligned(X, 4)) || !aligned(x_scale, 4) || !aligned(x_sum, 4))
+        return fail(BT_ERR_ALIGN, "X, x_scale and x_sum must be 4-byte aligned");
+    if (Xq && !aligned(Xq, 16))
+        return fail(BT_ERR_ALIGN, "Xq must be 16-byte aligned");
+    return hip_status(bt::launch_quant_act(X, M, K, bt_act_row_bytes(K), Xq, x_scale, x_sum,
+                                           static_cast<hipStream_t>(stream)),
+                      "bt_quant_act launch");
+}
+
+bt_status bt_ternary_gemv_algo(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
+                               const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                               int32_t algo, void *stream)
+{
+    if (bt_status s = check_product(Wp, w_scale, Xq, x_scale, x_sum, M, N, K, Y, acc))
+        return s;
+    if (M > BT_GEMV_MAX_M)
+        return fail(BT_ERR_UNSUPPORTED, "gemv takes M <= %d (got %lld); use bt_ternary_gemm", BT_GEMV_MAX_M,
+                    (long long)M);
+    if (algo != BT_GEMV_AUTO && algo != BT_GEMV_DOT4 && algo != BT_GEMV_MFMA)
+        return fail(BT_ERR_UNSUPPORTED, "unknown gemv algo %d", (int)algo);
+    if (M == 0 || N == 0)
+        return ok();
+    if (algo == BT_GEMV_AUTO)
+        algo = (M <= 2) ? BT_GEMV_DOT4 : BT_GEMV_MFMA;
+    if (algo == BT_GEMV_DOT4 && M > 4)
+        return fail(BT_ERR_UNSUPPORTED, "dot4 gemv takes M <= 4 (got %lld)", (long long)M);
+    const int64_t ldq = bt_act_row_bytes(K);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint4 *W = static_cast<const uint4 *>(Wp);
+    hipError_t e = (algo == BT_GEMV_DOT4)
+                       ? bt::launch_gemv_dot4(W, w_scale, Xq, ldq, x_scale, x_sum, M, N, K, Y, acc, s)
+                       : bt::launch_gemv_mfma(W, w_scale, Xq, ldq, x_scale, x_sum, M, N, K, Y, acc, s);
+    return hip_status(e, "bt_ternary_gemv launch");
+}
+
+bt_status bt_ternary_gemv(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
+                          const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *stream)
+{
+    return bt_ternary_gemv_algo(Wp, w_scale, Xq, x_scale, x_sum, M, N, K, Y, acc, BT_GEMV_AUTO, stream);
+}
+
+bt_status bt_ternary_gemm(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
+                          const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *stream)
+{
+    if (bt_status s = check_product(Wp, w_scale, Xq, x_scale, x_sum, M, N, K, Y, acc))
+        return s;
+    if (M == 0 || N == 0)
+        return ok();
+    const int64_t ldq = bt_act_row_bytes(K);
+    return hip_status(bt::launch_gemm(static_cast<const uint4 *>(Wp), w_scale, Xq, ldq, x_scale, x_sum, M, N, K, Y,
+                                      acc, static_cast<hipStream_t>(stream)),
+                      "bt_ternary_gemm launch");
+}
+
+const char *bt_status_str(bt_status s)
+{
+    switch (s) {
+    case BT_OK: return "BT_OK";
+    case BT_ERR_NULL: return "BT_ERR_NULL";
+    case BT_ERR_SHAPE: return "BT_ERR_SHAPE";
+    case BT_ERR_UNSUPPORTED: return "BT_ERR_UNSUPPORTED";
+    case BT_ERR_ALIGN: return "BT_ERR_ALIGN";
+    case BT_ERR_HIP: return "BT_ERR_HIP";
+    default: return "BT_ERR_UNKNOWN";
+    }
+}
+
+const char *bt_last_error(void) { return g_err; }
+
+}  // extern "C"

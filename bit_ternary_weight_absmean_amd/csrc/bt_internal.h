@@ -1,0 +1,56 @@
+// Internal helpers shared by the libbt kernels (gfx950 / CDNA4, wave64).
+//
+// Packed weight layout (matches the public description in bt.h):
+//   chunk (rb, c) = rows 64*rb .. +63, k = 64*c .. +63, 1024 bytes at
+//   ((rb * KC) + c) * 1024 with KC = Kp / 64. Row r of a chunk is one uint4 at
+//   uint4 index ((rb * KC) + c) * 64 + r. Word j of that uint4 holds codes for
+//   k = 64c + 16j + b, b = 0..15, code b at bit 8*(b&3) + 2*(b>>2); code = t + 1.
+//
+// Why this bit order: masking a word with 0x03030303 << 2s (s = 0..2), or
+// (word >> 2) & 0x30303030 for s = 3, leaves four int8 lanes that each hold one
+// code of four CONSECUTIVE k (k = 64c + 16j + 4s + e, byte e), times 4^s (s <= 2)
+// or 16 (s = 3). Each such dword feeds one v_dot4 / one MFMA operand dword
+// against the matching dword of int8 activations without any shift, and the
+// per-mask accumulators are recombined exactly as a1 + (a4 >> 2) + (a16 >> 4).
+// With offset codes (t + 1 in {0,1,2}) the bytes are non-negative and small
+// (<= 32), so the signed int8 dot product is exact; the "+1" is removed at the
+// end by subtracting sum_k q (computed once per token by the quantizer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bt {
+
+constexpr int kRowsPerChunk = 64;   // weight rows per packed chunk (one per lane)
+constexpr int kKPerChunk = 64;      // k per packed chunk (16 bytes per row)
+constexpr uint32_t kPadWord = 0x55555555u;  // sixteen codes "1" = sixteen zero weights
+
+constexpr uint32_t kMask0 = 0x03030303u;  // codes b = e        (weight 1)
+constexpr uint32_t kMask1 = 0x0C0C0C0Cu;  // codes b = 4 + e    (weight 4)
+constexpr uint32_t kMask2 = 0x30303030u;  // codes b = 8 + e    (weight 16); also (w>>2) for b = 12+e
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Wave-uniform value the compiler can keep in an SGPR.
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Launchers (each returns hipGetLastError() after the launch).
+hipError_t launch_pack(const float *W, int64_t N, int64_t K, uint4 *Wp, float *gamma, double *rowsum,
+                       hipStream_t s);
+hipError_t launch_unpack(const uint4 *Wp, int64_t N, int64_t K, int8_t *T, hipStream_t s);
+hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int64_t ldq, int8_t *Xq, float *sx,
+                            int32_t *xsum, hipStream_t s);
+hipError_t launch_gemv_dot4(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq,
+                            const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
+                            int32_t *acc, hipStream_t s);
+hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq,
+                            const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
+                            int32_t *acc, hipStream_t s);
+hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
+                       const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                       hipStream_t s);
+
+}  // namespace bt

@@ -1,0 +1,123 @@
+// Fused per-token absmax int8 activation quantizer: one workgroup per token row.
+//
+// BitNet GPU guide ("How to Run BitNet Inference on GPU Using CUDA Kernels"),
+// "Understanding the Two-Phase Architecture": activations are quantized to INT8
+// with their own scales right before the INT8 x INT2 product; "bit-floor" page,
+// "What's inside" (scale.rs): absmax scale, quantized on the fly before each GEMV.
+//
+// Per row m: a = max_k |x| (exact, order-free), inv = 127.0f / a (IEEE fp32
+// division, correctly rounded), q = clamp(rint(x * inv), -127, 127) (round half to
+// even), s_x = a / 127.0f and sum_k q. The int8 row is written with stride ldq
+// (K rounded up to 64) and zero padding, four codes per 32-bit store.
+#include "bt_internal.h"
+
+namespace bt {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+__device__ inline int wave_sum(int v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ inline int quant_one(float x, float inv)
+{
+    float r = rintf(x * inv);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_act(const float *__restrict__ X, int64_t K, int64_t ldq,
+                                                        int8_t *__restrict__ Xq, float *__restrict__ sx,
+                                                        int32_t *__restrict__ xsum)
+{
+    __shared__ float red_f[kThreads / 64];
+    __shared__ int red_i[kThreads / 64];
+    const int tid = threadIdx.x;
+    const int64_t m = blockIdx.x;
+    const float *x = X + m * K;
+    const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+
+    // Pass 1: absmax.
+    float amax = 0.0f;
+    if (vec) {
+        for (int64_t k = 4 * tid; k < K; k += 4 * kThreads) {
+            const float4 v = *reinterpret_cast<const float4 *>(x + k);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+    } else {
+        for (int64_t k = tid; k < K; k += kThreads)
+            amax = fmaxf(amax, fabsf(x[k]));
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0)
+        red_f[tid >> 6] = amax;
+    __syncthreads();
+    amax = red_f[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w)
+        amax = fmaxf(amax, red_f[w]);
+
+    // Pass 2: quantize (the row is re-read from cache), pad with zeros, sum q.
+    const bool zero = (amax == 0.0f);
+    const float inv = zero ? 0.0f : 127.0f / amax;
+    int8_t *q = Xq + m * ldq;
+    int sum = 0;
+    for (int64_t k = 4 * tid; k < ldq; k += 4 * kThreads) {
+        int e0 = 0, e1 = 0, e2 = 0, e3 = 0;
+        if (!zero) {
+            if (vec && k + 4 <= K) {
+                const float4 v = *reinterpret_cast<const float4 *>(x + k);
+                e0 = quant_one(v.x, inv);
+                e1 = quant_one(v.y, inv);
+                e2 = quant_one(v.z, inv);
+                e3 = quant_one(v.w, inv);
+            } else {
+                if (k + 0 < K) e0 = quant_one(x[k + 0], inv);
+                if (k + 1 < K) e1 = quant_one(x[k + 1], inv);
+                if (k + 2 < K) e2 = quant_one(x[k + 2], inv);
+                if (k + 3 < K) e3 = quant_one(x[k + 3], inv);
+            }
+        }
+        sum += e0 + e1 + e2 + e3;
+        const uint32_t packed = (uint32_t)(e0 & 0xff) | ((uint32_t)(e1 & 0xff) << 8) |
+                                ((uint32_t)(e2 & 0xff) << 16) | ((uint32_t)(e3 & 0xff) << 24);
+        *reinterpret_cast<uint32_t *>(q + k) = packed;
+    }
+    sum = wave_sum(sum);
+    if ((tid & 63) == 0)
+        red_i[tid >> 6] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int total = 0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w)
+            total += red_i[w];
+        sx[m] = zero ? 0.0f : amax / 127.0f;
+        xsum[m] = total;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int64_t ldq, int8_t *Xq, float *sx,
+                            int32_t *xsum, hipStream_t s)
+{
+    if (M > 0)
+        hipLaunchKernelGGL(k_quant_act, dim3((unsigned)M), dim3(kThreads), 0, s, X, K, ldq, Xq, sx, xsum);
+    return hipGetLastError();
+}
+
+}  // namespace bt

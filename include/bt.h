@@ -1,0 +1,169 @@
+/*
+ * bt.h -- C ABI of libbt.so, the MI355X (gfx950) BitNet b1.58 W1.58A8 ternary
+ * linear layer.
+ *
+ * The method (BitNet b1.58, as described on the pages this library follows):
+ *   weights   W [N,K] fp32 -> gamma = mean|W| (one fp32 scale per matrix) and
+ *             t = RoundClip(W / gamma, -1, 1) in {-1, 0, +1}, packed 2 bits each;
+ *   inputs    X [M,K] fp32 -> per token m: a = max_k |X[m,k]|,
+ *             q = clamp(rint(X * (127 / a)), -127, 127) int8, s_x = a / 127;
+ *   product   acc[m,n] = sum_k t[n,k] * q[m,k] in int32 (add, subtract or skip);
+ *   output    Y[m,n] = fp32(acc[m,n]) * (gamma * s_x[m]).
+ * Every integer result (codes, q, sum q, acc) is exact; Y carries two fp32 roundings.
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or keeps them. Scales stay on the device (no host readback).
+ *  - `stream` is a hipStream_t (NULL = the null stream). Work is only enqueued:
+ *    calls return before the GPU finishes, never synchronize, and can be captured
+ *    into a HIP graph. A fault inside a kernel surfaces at the caller's next sync.
+ *  - Arguments are validated on the host before any HIP call; on failure nothing
+ *    is enqueued and a non-zero bt_status is returned (bt_last_error() says why).
+ *  - Matrices are row-major. M = tokens, N = output features (rows of W),
+ *    K = input features. 0 <= M, N; 0 <= K <= BT_MAX_K. M == 0 or N == 0 is a no-op.
+ *  - Non-finite inputs are outside the contract; the results are then unspecified
+ *    (but the kernels still stay in bounds).
+ *  - Calls on different streams may run concurrently; a call reads only its
+ *    inputs and writes only its outputs. The library holds no mutable global state
+ *    other than a thread-local error string.
+ */
+#ifndef BT_H
+#define BT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t bt_status;
+
+#define BT_OK 0
+#define BT_ERR_NULL 1        /* a required pointer is NULL (or both outputs are) */
+#define BT_ERR_SHAPE 2       /* a dimension is negative or above its limit      */
+#define BT_ERR_UNSUPPORTED 3 /* valid arguments the chosen kernel cannot take    */
+#define BT_ERR_ALIGN 4       /* a pointer lacks the alignment stated below      */
+#define BT_ERR_HIP 5         /* the HIP runtime rejected a launch               */
+
+/* K is bounded so that |acc| <= 127*K < 2^24: acc then converts to fp32 exactly. */
+#define BT_MAX_K 131072
+/* Largest token count the decode GEMV entry point accepts. */
+#define BT_GEMV_MAX_M 16
+
+/* Decode GEMV kernel choices for bt_ternary_gemv_algo. */
+#define BT_GEMV_AUTO 0 /* pick by M from the library's launch table             */
+#define BT_GEMV_DOT4 1 /* one lane per weight row, v_dot4 with the x chunk in SGPRs */
+#define BT_GEMV_MFMA 2 /* int8 MFMA 16x16x64, 64 weight rows per wave             */
+
+/*
+ * Packed weight layout (the library's own format, produced by bt_pack_weights):
+ *   Np = N rounded up to 64, Kp = K rounded up to 64. The matrix is cut into
+ *   1024-byte chunks of 64 rows x 64 k; chunk (rb, c) covers rows 64*rb .. +63 and
+ *   k = 64*c .. +63 and starts at byte ((rb * Kp/64) + c) * 1024. Row r of the chunk
+ *   is the 16 bytes at offset 16*r, i.e. 4 little-endian 32-bit words; word j holds
+ *   the 16 codes of k = 64*c + 16*j + b (b = 0..15), code b at bits
+ *   8*(b%4) + 2*(b/4) .. +1. A code is t + 1 (0 = -1, 1 = 0, 2 = +1). Padding
+ *   rows and columns hold code 1 (weight 0). Size: Np * Kp / 4 bytes.
+ */
+size_t bt_packed_weight_bytes(int64_t N, int64_t K);
+
+/* Row stride, in bytes, of the int8 activation matrix Xq: K rounded up to 64.
+ * Bytes k >= K of each row are zero (bt_quant_act writes them). */
+int64_t bt_act_row_bytes(int64_t K);
+
+/* Workspace, in bytes, that bt_pack_weights needs (fp64 per-row |W| sums). */
+size_t bt_pack_workspace_bytes(int64_t N, int64_t K);
+
+/*
+ * bt_pack_weights -- absmean ternarization and 2-bit packing of one weight matrix
+ * (once per matrix, offline). Follows the "bit-floor" page, "What's inside"
+ * (pack.rs: mean-abs threshold zero-suppression for ternary weights) and the
+ * "BitCompute" page, "Future Roadmap" (four 1.58-bit weights per byte).
+ *   W         [N,K] fp32, row-major, 16-byte aligned, read only.
+ *   Wp        output, bt_packed_weight_bytes(N,K) bytes, 16-byte aligned.
+ *   w_scale   output, one fp32: gamma = fp32(sum_n sum_k |W| / (N*K)) where each
+ *             row is summed k = 0..K-1 in fp64 and the row sums n = 0..N-1 in fp64
+ *             (this fixed order makes gamma reproducible bit for bit).
+ *             Codes: t = +1 if w > gamma/2, -1 if w < -gamma/2, else 0.
+ *   workspace bt_pack_workspace_bytes(N,K) bytes of device scratch, 8-byte aligned;
+ *             contents on entry are ignored; it may be reused after the call's
+ *             kernels complete (stream order).
+ * N == 0 or K == 0 writes gamma = 0 and nothing else.
+ */
+bt_status bt_pack_weights(const float *W, int64_t N, int64_t K, void *Wp, float *w_scale,
+                          void *workspace, void *stream);
+
+/*
+ * bt_unpack_weights -- inverse of the packing (a test and inspection aid):
+ *   T [N,K] int8 receives t in {-1, 0, +1}. Wp 16-byte aligned.
+ */
+bt_status bt_unpack_weights(const void *Wp, int64_t N, int64_t K, int8_t *T, void *stream);
+
+/*
+ * bt_quant_act -- fused per-token absmax int8 quantization, one pass per token.
+ * Follows the BitNet GPU guide ("How to Run BitNet Inference on GPU Using CUDA
+ * Kernels"), section "Understanding the Two-Phase Architecture" (inputs quantized
+ * to INT8 with their own scales before the INT8 x INT2 kernel), and the "bit-floor"
+ * page, "What's inside" (scale.rs: absmax, quantized before each GEMV).
+ *   X        [M,K] fp32 row-major, 4-byte aligned (16-byte aligned rows are faster).
+ *   Xq       output [M, bt_act_row_bytes(K)] int8, 16-byte aligned; bytes k >= K
+ *            of every row are written as 0.
+ *   x_scale  output [M] fp32: s_x = a / 127 (fp32 division), 0 for an all-zero row.
+ *   x_sum    output [M] int32: sum_k q[m,k] (needed by the GEMV/GEMM).
+ * q = clamp(rint(x * inv), -127, 127) with inv = 127.0f / a (correctly rounded fp32
+ * division, fp32 multiply, round half to even); an all-zero row gives q = 0.
+ */
+bt_status bt_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale,
+                       int32_t *x_sum, void *stream);
+
+/*
+ * bt_ternary_gemv -- decode product for 1 <= M <= BT_GEMV_MAX_M tokens: the integer
+ * ternary dot product with the scale epilogue fused. Follows the "bit-floor" page,
+ * "The core math" (integer inner loop, one floating-point scale multiply at the end)
+ * and the "BitCompute" page, "Features" (ternary weights make the product add /
+ * subtract / skip).
+ *   Wp       packed weights from bt_pack_weights(N, K).
+ *   w_scale  device pointer to gamma.
+ *   Xq, x_scale, x_sum   from bt_quant_act(M, K) (Xq rows of bt_act_row_bytes(K)
+ *            bytes with zero padding).
+ *   Y        output [M,N] fp32 or NULL; Y[m,n] = fp32(acc) * (gamma * s_x[m]).
+ *   acc      output [M,N] int32 or NULL: the exact accumulator sum_k t*q.
+ *   Y and acc may not both be NULL. Y and acc need 4-byte alignment. With K == 0
+ *   (an empty dot product: acc = 0) Wp and Xq may be NULL.
+ * Returns BT_ERR_UNSUPPORTED for M > BT_GEMV_MAX_M (use bt_ternary_gemm).
+ */
+bt_status bt_ternary_gemv(const void *Wp, const float *w_scale, const int8_t *Xq,
+                          const float *x_scale, const int32_t *x_sum, int64_t M, int64_t N,
+                          int64_t K, float *Y, int32_t *acc, void *stream);
+
+/* bt_ternary_gemv with an explicit kernel choice (BT_GEMV_AUTO / _DOT4 / _MFMA).
+ * BT_GEMV_DOT4 takes M <= 4; both return bit-identical acc and Y. */
+bt_status bt_ternary_gemv_algo(const void *Wp, const float *w_scale, const int8_t *Xq,
+                               const float *x_scale, const int32_t *x_sum, int64_t M, int64_t N,
+                               int64_t K, float *Y, int32_t *acc, int32_t algo, void *stream);
+
+/*
+ * bt_ternary_gemm -- prefill product for any M >= 1 on int8 MFMA: the packed
+ * weight tiles are unpacked in registers straight into MFMA operands, the int8
+ * activation tiles are staged in LDS, and the scale epilogue is fused. Same
+ * arguments and results as bt_ternary_gemv, with no limit on M. Follows the BitNet
+ * GPU guide, "Key Components and Source Code Architecture" (prefill is the
+ * compute-bound phase) and the "BitCompute" page, "Future Roadmap" (moving the
+ * ternary product onto the matrix cores).
+ */
+bt_status bt_ternary_gemm(const void *Wp, const float *w_scale, const int8_t *Xq,
+                          const float *x_scale, const int32_t *x_sum, int64_t M, int64_t N,
+                          int64_t K, float *Y, int32_t *acc, void *stream);
+
+/* Static text for a status code. */
+const char *bt_status_str(bt_status s);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char *bt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BT_H */

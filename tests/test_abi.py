@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports every function include/bt.h
+declares, sizes its buffers as documented, and rejects bad arguments on the host
+before any HIP call (so these run on a CPU-only machine)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_ternary_weight_absmean_amd as bt
+from bit_ternary_weight_absmean_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bt.h")
+
+BT_OK, BT_ERR_NULL, BT_ERR_SHAPE, BT_ERR_UNSUPPORTED, BT_ERR_ALIGN, BT_ERR_HIP = range(6)
+FAKE = 0x10000  # an aligned, never-dereferenced address: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    L = bt.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_built_for_gfx950():
+    data = open(_lib.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_sizes():
+    L = bt.lib()
+    assert L.bt_packed_weight_bytes(512, 256) == 512 * 256 // 4
+    assert L.bt_packed_weight_bytes(3840, 2560) == 2_457_600
+    assert L.bt_packed_weight_bytes(57344, 8192) == 117_440_512
+    assert L.bt_packed_weight_bytes(100, 300) == 128 * 320 // 4  # padded to 64 x 64
+    assert L.bt_packed_weight_bytes(0, 300) == 0
+    assert L.bt_act_row_bytes(2560) == 2560
+    assert L.bt_act_row_bytes(300) == 320
+    assert L.bt_act_row_bytes(1) == 64
+    assert L.bt_act_row_bytes(0) == 0
+    assert L.bt_pack_workspace_bytes(3, 5) == 256
+    assert L.bt_pack_workspace_bytes(100, 5) == 1024
+
+
+def _gemv(L, *, Wp=FAKE, ws=FAKE, Xq=FAKE, sx=FAKE, xsum=FAKE, M=1, N=64, K=64, Y=FAKE, acc=0, algo=0):
+    return L.bt_ternary_gemv_algo(Wp, ws, Xq, sx, xsum, M, N, K, Y, acc, algo, None)
+
+
+def test_product_validation():
+    L = bt.lib()
+    assert _gemv(L, Y=0, acc=0) == BT_ERR_NULL
+    assert _gemv(L, Wp=0) == BT_ERR_NULL
+    assert _gemv(L, xsum=0) == BT_ERR_NULL
+    assert _gemv(L, M=-1) == BT_ERR_SHAPE
+    assert _gemv(L, K=-5) == BT_ERR_SHAPE
+    assert _gemv(L, K=131073) == BT_ERR_SHAPE
+    assert _gemv(L, M=17) == BT_ERR_UNSUPPORTED
+    assert _gemv(L, M=5, algo=1) == BT_ERR_UNSUPPORTED
+    assert _gemv(L, algo=7) == BT_ERR_UNSUPPORTED
+    assert _gemv(L, Wp=FAKE + 4) == BT_ERR_ALIGN
+    assert _gemv(L, Xq=FAKE + 8) == BT_ERR_ALIGN
+    assert _gemv(L, Y=FAKE + 2) == BT_ERR_ALIGN
+    assert b"Y and acc" in _reason(L, lambda: _gemv(L, Y=0, acc=0))
+    # M == 0 or N == 0 is a no-op that succeeds without touching the device
+    assert _gemv(L, M=0) == BT_OK
+    assert _gemv(L, N=0) == BT_OK
+    assert L.bt_ternary_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, FAKE, 0, None) == BT_OK
+    assert L.bt_ternary_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 64, 0, 0, None) == BT_ERR_NULL
+    assert L.bt_ternary_gemm(FAKE + 1, FAKE, FAKE, FAKE, FAKE, 3, 64, 64, FAKE, 0, None) == BT_ERR_ALIGN
+
+
+def _reason(L, call):
+    call()
+    return L.bt_last_error()
+
+
+def test_pack_and_quant_validation():
+    L = bt.lib()
+    assert L.bt_pack_weights(FAKE, 4, 4, FAKE, 0, FAKE, None) == BT_ERR_NULL
+    assert L.bt_pack_weights(0, 4, 4, FAKE, FAKE, FAKE, None) == BT_ERR_NULL
+    assert L.bt_pack_weights(FAKE, 4, 4, FAKE, FAKE, 0, None) == BT_ERR_NULL
+    assert L.bt_pack_weights(FAKE, -1, 4, FAKE, FAKE, FAKE, None) == BT_ERR_SHAPE
+    assert L.bt_pack_weights(FAKE + 4, 4, 4, FAKE, FAKE, FAKE, None) == BT_ERR_ALIGN
+    assert L.bt_pack_weights(FAKE, 4, 4, FAKE, FAKE, FAKE + 4, None) == BT_ERR_ALIGN
+    assert L.bt_unpack_weights(0, 4, 4, FAKE, None) == BT_ERR_NULL
+    assert L.bt_unpack_weights(FAKE, 0, 4, 0, None) == BT_OK
+    assert L.bt_quant_act(FAKE, -2, 4, FAKE, FAKE, FAKE, None) == BT_ERR_SHAPE
+    assert L.bt_quant_act(FAKE, 2, 4, FAKE, 0, FAKE, None) == BT_ERR_NULL
+    assert L.bt_quant_act(FAKE, 2, 4, FAKE + 4, FAKE, FAKE, None) == BT_ERR_ALIGN
+    assert L.bt_quant_act(FAKE + 2, 2, 4, FAKE, FAKE, FAKE, None) == BT_ERR_ALIGN
+    assert L.bt_quant_act(FAKE, 0, 4, 0, 0, 0, None) == BT_OK
+
+
+def test_status_strings():
+    L = bt.lib()
+    names = [L.bt_status_str(i).decode() for i in range(6)]
+    assert names == ["BT_OK", "BT_ERR_NULL", "BT_ERR_SHAPE", "BT_ERR_UNSUPPORTED", "BT_ERR_ALIGN", "BT_ERR_HIP"]
+    assert L.bt_status_str(99).decode() == "BT_ERR_UNKNOWN"
+
+
+def test_python_error_type():
+    with pytest.raises(bt.BTError) as e:
+        _lib.check(BT_ERR_SHAPE)
+    assert e.value.name == "BT_ERR_SHAPE"
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    """The package never imports the oracle, and its sources name no CPU fallback."""
+    pkg = os.path.dirname(bt.__file__)
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "import oracle" not in src and "from oracle" not in src, fn

@@ -1,0 +1,348 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: gamma, ternary codes, int8 activations, s_x, sum q and the int32 accumulator
+bit-exact; Y within |dY| <= 1e-5 |Y| + 1e-6. Inputs come from the seeded generators
+in ``bit_ternary_weight_absmean_amd.synth``; expected values only from ``oracle``.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import bit_ternary_weight_absmean_amd as bt
+from bit_ternary_weight_absmean_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def note(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def tol_ok(y, ref):
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return bool(np.all(np.abs(y - ref) <= 1e-5 * np.abs(ref) + 1e-6))
+
+
+def f32_bits(x):
+    return np.asarray(x, np.float32).view(np.uint32)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def gpu_pack(W):
+    pw = bt.pack_weights(to_dev(W))
+    return pw
+
+
+def gpu_quant(X):
+    return bt.quant_act(to_dev(X))
+
+
+def oracle_layer(W, X):
+    return oracle.linear(W, X)
+
+
+def check_product(pw, q, ref, M, N, fn, **kw):
+    Y, acc = fn(pw, q, want_y=True, want_acc=True, **kw)
+    torch.cuda.synchronize()
+    acc = acc.cpu().numpy()
+    Y = Y.cpu().numpy()
+    assert acc.shape == (M, N)
+    bad = np.argwhere(acc != ref["acc"])
+    assert bad.size == 0, f"{len(bad)} acc mismatches, first at {bad[:5].tolist()}"
+    assert tol_ok(Y, ref["Y"])
+
+
+# ------------------------------------------------------------------- pack
+PACK_SHAPES = [(1, 1), (3, 7), (64, 64), (100, 300), (512, 256), (65, 129), (2560, 2560), (3840, 2560)]
+
+
+@pytest.mark.parametrize("N,K", PACK_SHAPES)
+def test_pack_gamma_and_codes(N, K):
+    note(f"pack N={N} K={K}")
+    W = synth.gaussian((N, K), 7000 + N + K, 0.02)
+    pw = gpu_pack(W)
+    T = bt.unpack_weights(pw)
+    torch.cuda.synchronize()
+    g_ref = oracle.absmean(W)
+    assert f32_bits(pw.scale.cpu().numpy()[0]) == f32_bits(g_ref)
+    np.testing.assert_array_equal(T.cpu().numpy(), oracle.ternarize(W, g_ref))
+
+
+def test_pack_ties_and_padding():
+    """Weights exactly at +-gamma/2 pack to 0; padded rows/columns are never visible."""
+    note("pack ties")
+    W = np.array([[0.75, -0.25, 0.25, 0.75]], np.float32)
+    pw = gpu_pack(W)
+    np.testing.assert_array_equal(bt.unpack_weights(pw).cpu().numpy(), [[1, 0, 0, 1]])
+    assert pw.scale.item() == 0.5
+    raw = pw.data.cpu().numpy().view(np.uint32)
+    # chunk 0, row 0: word 0 holds codes k=0..15 -> codes 2,1,1,2 then padding code 1
+    assert raw.size == 64 * 64 // 16
+    assert np.all(raw[4:] == 0x55555555)  # rows 1..63 are all padding
+
+
+def test_pack_zero_matrix():
+    note("pack zero")
+    W = np.zeros((70, 90), np.float32)
+    pw = gpu_pack(W)
+    assert pw.scale.item() == 0.0
+    assert not bt.unpack_weights(pw).cpu().numpy().any()
+
+
+# ------------------------------------------------------------------ quant
+QUANT_SHAPES = [(1, 1), (1, 7), (3, 300), (128, 256), (1, 2560), (1, 28672), (5, 6912), (2048, 2560)]
+
+
+@pytest.mark.parametrize("M,K", QUANT_SHAPES)
+def test_quant_act(M, K):
+    note(f"quant M={M} K={K}")
+    X = synth.gaussian((M, K), 8000 + M + K)
+    if M >= 3:
+        X[1] = 0.0  # an all-zero token
+    Xq, sx, xsum = gpu_quant(X)
+    torch.cuda.synchronize()
+    Q, s_ref, qs_ref = oracle.quant_act(X)
+    Xq = Xq.cpu().numpy()
+    assert Xq.shape == (M, bt.act_row_bytes(K))
+    np.testing.assert_array_equal(Xq[:, :K], Q)
+    assert not Xq[:, K:].any()
+    np.testing.assert_array_equal(f32_bits(sx.cpu().numpy()), f32_bits(s_ref))
+    np.testing.assert_array_equal(xsum.cpu().numpy(), qs_ref)
+
+
+def test_quant_hand_ties():
+    note("quant ties")
+    X = np.array([[127.0, 62.5, -0.5, 1.5], [127.0, -1.5, -2.5, 3.5], [1.0, -2.0, 0.5, 0.25]], np.float32)
+    Xq, sx, xsum = gpu_quant(X)
+    np.testing.assert_array_equal(Xq.cpu().numpy()[:, :4], [[127, 62, 0, 2], [127, -2, -2, 4], [64, -127, 32, 16]])
+    np.testing.assert_array_equal(xsum.cpu().numpy(), [191, 127, -15])
+
+
+def test_quant_unaligned_rows():
+    """K not a multiple of 4 and an input at a 4-byte (not 16-byte) offset."""
+    note("quant unaligned")
+    X = synth.gaussian((4, 4 * 133 + 1), 8100)
+    big = torch.zeros(X.size + 1, dtype=torch.float32, device=DEV)
+    big[1:] = to_dev(X.ravel())
+    Xd = big[1:].view(4, -1)
+    Xq, sx, xsum = bt.quant_act(Xd)
+    Q, s_ref, qs_ref = oracle.quant_act(X)
+    np.testing.assert_array_equal(Xq.cpu().numpy()[:, :X.shape[1]], Q)
+    np.testing.assert_array_equal(xsum.cpu().numpy(), qs_ref)
+
+
+# -------------------------------------------------------------- products
+SMALL = [(1, 1, 1), (1, 100, 300), (2, 130, 129), (3, 65, 1000), (4, 512, 256), (5, 200, 700),
+         (8, 64, 64), (16, 300, 517), (16, 1000, 2560)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+@pytest.mark.parametrize("algo", [bt.GEMV_DOT4, bt.GEMV_MFMA, bt.GEMV_AUTO])
+def test_gemv_small(M, N, K, algo):
+    if algo == bt.GEMV_DOT4 and M > 4:
+        pytest.skip("dot4 takes M <= 4")
+    note(f"gemv algo={algo} M={M} N={N} K={K}")
+    W = synth.gaussian((N, K), 9000 + N, 0.02)
+    X = synth.gaussian((M, K), 9500 + M)
+    ref = oracle_layer(W, X)
+    check_product(gpu_pack(W), gpu_quant(X), ref, M, N, bt.ternary_gemv, algo=algo)
+
+
+GEMM_SMALL = [(1, 64, 64), (17, 100, 300), (128, 512, 256), (129, 130, 129), (300, 200, 517), (64, 1000, 2560)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SMALL)
+def test_gemm_small(M, N, K):
+    note(f"gemm M={M} N={N} K={K}")
+    W = synth.gaussian((N, K), 9100 + N, 0.02)
+    X = synth.gaussian((M, K), 9600 + M)
+    ref = oracle_layer(W, X)
+    check_product(gpu_pack(W), gpu_quant(X), ref, M, N, bt.ternary_gemm)
+
+
+def test_tiny_workload_all_paths():
+    """The tiny matmul workload (X [128,256], W [512,256], seed 0): gemm at M=128, gemv per token."""
+    note("tiny workload")
+    W, X = synth.tiny_matmul()
+    ref = oracle_layer(W, X)
+    pw, q = gpu_pack(W), gpu_quant(X)
+    check_product(pw, q, ref, 128, 512, bt.ternary_gemm)
+    for m0 in (0, 16, 112):
+        sub = {"acc": ref["acc"][m0:m0 + 16], "Y": ref["Y"][m0:m0 + 16]}
+        qs = (q[0][m0:m0 + 16], q[1][m0:m0 + 16], q[2][m0:m0 + 16])
+        check_product(pw, qs, sub, 16, 512, bt.ternary_gemv, algo=bt.GEMV_MFMA)
+    for m0 in (0, 77, 127):
+        sub = {"acc": ref["acc"][m0:m0 + 1], "Y": ref["Y"][m0:m0 + 1]}
+        qs = (q[0][m0:m0 + 1], q[1][m0:m0 + 1], q[2][m0:m0 + 1])
+        check_product(pw, qs, sub, 1, 512, bt.ternary_gemv, algo=bt.GEMV_DOT4)
+
+
+# --------------------------------------------- full-size layer shapes
+@pytest.mark.parametrize("j,name,N,K", [(j, *s) for j, s in enumerate(synth.SHAPES_2B)])
+def test_2b_decode_shapes_full(j, name, N, K):
+    """2B decode layer shapes at M=1 (every output compared), in the launch the benchmark uses."""
+    note(f"2B {name} N={N} K={K}")
+    W = synth.layer_weight(synth.CFG_2B_DECODE, 0, j, N, K)
+    X = synth.layer_activation(synth.CFG_2B_DECODE, j, 1, K)
+    ref = oracle_layer(W, X)
+    pw, q = gpu_pack(W), gpu_quant(X)
+    assert f32_bits(pw.scale.cpu().numpy()[0]) == f32_bits(ref["gamma"])
+    for algo in (bt.GEMV_AUTO, bt.GEMV_DOT4, bt.GEMV_MFMA):
+        check_product(pw, q, ref, 1, N, bt.ternary_gemv, algo=algo)
+    # 2B prefill at M=256 on the same weight (gemm)
+    X2 = synth.layer_activation(synth.CFG_2B_PREFILL, j, 256, K)
+    q2 = gpu_quant(X2)
+    Q2, s2, qs2 = oracle.quant_act(X2)
+    T = oracle.ternarize(W, ref["gamma"])
+    rows = np.arange(0, 256, 7)
+    acc_ref = oracle.ternary_matmul(T, Q2[rows])
+    Y2, acc2 = bt.ternary_gemm(pw, q2, want_acc=True)
+    acc2 = acc2.cpu().numpy()
+    np.testing.assert_array_equal(acc2[rows], acc_ref)
+    assert tol_ok(Y2.cpu().numpy()[rows], oracle.scale_epilogue(acc_ref, ref["gamma"], s2[rows]))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_7b_gate_up_decode(M):
+    note(f"7B gate_up M={M}")
+    j = 2
+    name, N, K = synth.SHAPES_7B[j]
+    W = synth.layer_weight(synth.CFG_7B_DECODE, 0, j, N, K)
+    X = synth.layer_activation(synth.CFG_7B_DECODE, j, M, K)
+    g = oracle.absmean(W)
+    T = oracle.ternarize(W, g)
+    assert abs(float(np.mean(T == 0)) - 0.3101) < 0.005  # "~1/3 zeros"
+    Q, s, qs = oracle.quant_act(X)
+    rows = np.arange(0, N, 5)
+    acc_ref = oracle.ternary_matmul(T[rows], Q)
+    pw, q = gpu_pack(W), gpu_quant(X)
+    for algo in ((bt.GEMV_AUTO, bt.GEMV_DOT4, bt.GEMV_MFMA) if M <= 4 else (bt.GEMV_AUTO, bt.GEMV_MFMA)):
+        Y, acc = bt.ternary_gemv(pw, q, want_acc=True, algo=algo)
+        np.testing.assert_array_equal(acc.cpu().numpy()[:, rows], acc_ref)
+        assert tol_ok(Y.cpu().numpy()[:, rows], oracle.scale_epilogue(acc_ref, g, s))
+
+
+def test_100b_down_decode_m16():
+    """The longest K (28672) at M = 16 on a 100B-class down projection, sampled rows."""
+    note("100B down M=16")
+    j, N, K = 3, 8192, 28672
+    W = synth.layer_weight(synth.CFG_100B_DECODE, 0, j, N, K)
+    X = synth.layer_activation(synth.CFG_100B_DECODE, j, 16, K)
+    g = oracle.absmean(W)
+    rows = np.arange(3, N, 11)
+    T = oracle.ternarize(W[rows], g)
+    Q, s, qs = oracle.quant_act(X)
+    acc_ref = oracle.ternary_matmul(T, Q)
+    pw, q = gpu_pack(W), gpu_quant(X)
+    assert f32_bits(pw.scale.cpu().numpy()[0]) == f32_bits(g)
+    for M, algo in ((16, bt.GEMV_MFMA), (1, bt.GEMV_DOT4), (1, bt.GEMV_MFMA)):
+        qm = (q[0][:M], q[1][:M], q[2][:M])
+        Y, acc = bt.ternary_gemv(pw, qm, want_acc=True, algo=algo)
+        np.testing.assert_array_equal(acc.cpu().numpy()[:, rows], acc_ref[:M])
+
+
+def test_2b_prefill_m2048_gate_up_sampled():
+    note("2B prefill M=2048 gate_up")
+    j = 2
+    name, N, K = synth.SHAPES_2B[j]
+    W = synth.layer_weight(synth.CFG_2B_PREFILL, 0, j, N, K)
+    X = synth.layer_activation(synth.CFG_2B_PREFILL, j, 2048, K)
+    g = oracle.absmean(W)
+    T = oracle.ternarize(W, g)
+    Q, s, qs = oracle.quant_act(X)
+    rows = np.concatenate([np.arange(0, 2048, 61), [2047]])
+    acc_ref = oracle.ternary_matmul(T, Q[rows])
+    pw, q = gpu_pack(W), gpu_quant(X)
+    Y, acc = bt.ternary_gemm(pw, q, want_acc=True)
+    np.testing.assert_array_equal(acc.cpu().numpy()[rows], acc_ref)
+    assert tol_ok(Y.cpu().numpy()[rows], oracle.scale_epilogue(acc_ref, g, s[rows]))
+
+
+# ------------------------------------------------ invariants and edges
+def test_negated_weights_negate_y_bitwise():
+    note("negate W")
+    W = synth.gaussian((300, 700), 9900, 0.02)
+    X = synth.gaussian((4, 700), 9901)
+    q = gpu_quant(X)
+    Y1, a1 = bt.ternary_gemv(gpu_pack(W), q, want_acc=True)
+    Y2, a2 = bt.ternary_gemv(gpu_pack(-W), q, want_acc=True)
+    np.testing.assert_array_equal(a2.cpu().numpy(), -a1.cpu().numpy())
+    np.testing.assert_array_equal(Y2.cpu().numpy(), -Y1.cpu().numpy())
+
+
+def test_zero_weights_and_empty_k():
+    note("zero W / K=0")
+    X = synth.gaussian((3, 100), 9902)
+    Y, acc = bt.ternary_gemv(gpu_pack(np.zeros((70, 100), np.float32)), gpu_quant(X), want_acc=True)
+    assert not acc.cpu().numpy().any() and not Y.cpu().numpy().any()
+    # K = 0: every accumulator is an empty sum
+    W0 = torch.zeros((70, 0), dtype=torch.float32, device=DEV)
+    pw0 = bt.pack_weights(W0)
+    q0 = bt.quant_act(torch.zeros((3, 0), dtype=torch.float32, device=DEV))
+    for fn in (bt.ternary_gemv, bt.ternary_gemm):
+        Y, acc = fn(pw0, q0, want_acc=True)
+        assert not acc.cpu().numpy().any() and not Y.cpu().numpy().any()
+
+
+def test_outputs_optional():
+    note("optional outputs")
+    W = synth.gaussian((128, 256), 9903, 0.02)
+    X = synth.gaussian((2, 256), 9904)
+    ref = oracle_layer(W, X)
+    pw, q = gpu_pack(W), gpu_quant(X)
+    Y, acc = bt.ternary_gemv(pw, q, want_y=False, want_acc=True)
+    assert Y is None
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    Y, acc = bt.ternary_gemm(pw, q, want_y=True, want_acc=False)
+    assert acc is None and tol_ok(Y.cpu().numpy(), ref["Y"])
+
+
+def test_error_paths_raise():
+    note("errors")
+    W = synth.gaussian((64, 64), 9905, 0.02)
+    X = synth.gaussian((17, 64), 9906)
+    pw, q = gpu_pack(W), gpu_quant(X)
+    with pytest.raises(bt.BTError) as e:
+        bt.ternary_gemv(pw, q)
+    assert e.value.name == "BT_ERR_UNSUPPORTED"
+
+
+def test_side_stream_and_graph_replay():
+    """Work enqueued on a non-default stream and captured in a HIP graph, replayed with new inputs."""
+    note("stream + graph")
+    N, K, M = 3840, 2560, 1
+    W = synth.gaussian((N, K), 9907, 0.02)
+    pw = gpu_pack(W)
+    T = oracle.ternarize(W, oracle.absmean(W))
+    xin = torch.zeros((M, K), dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q = bt.quant_act(xin)
+        Y, acc = bt.ternary_gemv(pw, q, want_acc=True)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        bt.quant_act(xin, out=q)
+        bt.ternary_gemv(pw, q, out_y=Y, out_acc=acc)
+    for rep in range(3):
+        X = synth.gaussian((M, K), 9910 + rep)
+        xin.copy_(to_dev(X))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        Q, sx, qs = oracle.quant_act(X)
+        acc_ref = oracle.ternary_matmul(T, Q)
+        np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+        eager_Y, eager_acc = bt.ternary_gemv(pw, bt.quant_act(to_dev(X)), want_acc=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(Y.cpu().numpy(), eager_Y.cpu().numpy())
