@@ -3,10 +3,12 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager] [--no-cpu-baseline]
 
 A step is one pass of the whole per-call hot path over one batch of synthetic input:
-for every resident weight matrix, quantize its activations (bt_quant_act) and run the
-ternary product with the fused scale epilogue (bt_ternary_gemv, or bt_ternary_gemm for
-prefill). Weight packing is offline and outside the timed region. Inputs are resident
-in HBM before timing starts. Prints ONE JSON line (rank 0, one GPU).
+for every resident weight matrix, quantize its fp32 activations per token to int8, run
+the integer ternary product and apply the scale epilogue -- one bt_ternary_linear call
+per matrix (a single fused kernel at decode sizes; bt_quant_act + bt_ternary_gemm for
+prefill). ``--split`` times the unfused route (bt_quant_act + bt_ternary_gemv/gemm as
+two launches) instead. Weight packing is offline and outside the timed region. Inputs
+are resident in HBM before timing starts. Prints ONE JSON line (one GPU).
 
 Workloads (``--workload``):
   2b_decode   (default) 2B-class decode, M = 1: 30 layers x {QKV 3840x2560, O 2560x2560,
@@ -45,6 +47,7 @@ def parse():
     p.add_argument("--workload", default="2b_decode", choices=["2b_decode", "7b_decode", "100b_decode", "2b_prefill"])
     p.add_argument("--m", type=int, default=None, help="tokens per call (default: 1 for decode, 2048 for prefill)")
     p.add_argument("--eager", action="store_true", help="launch kernels one by one instead of replaying a graph")
+    p.add_argument("--split", action="store_true", help="time bt_quant_act + product as two launches per matrix")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     p.add_argument("--calib-copy", action="store_true",
@@ -73,6 +76,12 @@ def gemv_bytes(M, N, K):
     """Algorithmic HBM bytes of one product call: 2-bit weights, int8 activations read,
     fp32 output written, gamma + s_x + sum q read."""
     return N * K // 4 + M * K + 4 * M * N + 4 + 8 * M
+
+
+def linear_bytes(M, N, K):
+    """Algorithmic HBM bytes of one fused decode call: 2-bit weights and fp32 activations
+    read, fp32 output written, gamma read."""
+    return N * K // 4 + 4 * M * K + 4 * M * N + 4
 
 
 def quant_bytes(M, K):
@@ -109,22 +118,31 @@ def run_gpu(args, spec):
     setup_s = time.time() - t0
     resident = sum(p.data.numel() for row in packed for p in row)
 
-    # Per-matrix-type activations and output buffers.
-    xs, qs, ys = [], [], []
+    # Per-matrix-type activations, output buffers and (route permitting) workspaces.
+    xs, qs, ys, wss = [], [], [], []
     for j, (_, N, K) in enumerate(shapes):
         X = torch.from_numpy(synth.layer_activation(cfg, j, M, K)).to(dev)
         xs.append(X)
         qs.append(bt.quant_act(X))
         ys.append(torch.empty((M, N), dtype=torch.float32, device=dev))
+        wb = bt.linear_workspace_bytes(M, N, K)
+        wss.append(torch.empty(wb, dtype=torch.uint8, device=dev) if wb else None)
     torch.cuda.synchronize()
 
     product = bt.ternary_gemm if spec["prefill"] else bt.ternary_gemv
 
+    if args.split:
+        def call(j, pw):
+            bt.quant_act(xs[j], out=qs[j])
+            product(pw, qs[j], out_y=ys[j])
+    else:
+        def call(j, pw):
+            bt.linear(xs[j], pw, out_y=ys[j], workspace=wss[j])
+
     def step():
         for row in packed:
             for j, pw in enumerate(row):
-                bt.quant_act(xs[j], out=qs[j])
-                product(pw, qs[j], out_y=ys[j])
+                call(j, pw)
 
     stream = torch.cuda.Stream(device=dev)
     graph = None
@@ -153,19 +171,24 @@ def run_gpu(args, spec):
         torch.cuda.synchronize()
         ms_step = start.elapsed_time(end) / args.steps
 
-        # Dominant kernel (the product) timed live: one event pair around every product
-        # launch, eager, on the stream the kernels run on.
+        # Dominant kernel (the product, with the quantizer fused in at decode sizes) timed
+        # live: one event pair around every product launch, eager, on the kernels' stream.
         per_shape_ms = [0.0] * len(shapes)
         reps = max(2, min(args.steps, 5))
         pairs = []
+        fused = not args.split and not spec["prefill"]
         for _ in range(reps):
             for row in packed:
                 for j, pw in enumerate(row):
-                    bt.quant_act(xs[j], out=qs[j])
+                    if not fused:
+                        bt.quant_act(xs[j], out=qs[j])
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record(stream)
-                    product(pw, qs[j], out_y=ys[j])
+                    if fused:
+                        bt.linear(xs[j], pw, out_y=ys[j], workspace=wss[j])
+                    else:
+                        product(pw, qs[j], out_y=ys[j])
                     e1.record(stream)
                     pairs.append((j, e0, e1))
         stream.synchronize()
@@ -177,22 +200,24 @@ def run_gpu(args, spec):
     step_bytes = 0
     step_ops = 0
     prod_bytes = 0
+    fused = not args.split and not spec["prefill"]
     for row in packed:
         for j, (_, N, K) in enumerate(shapes):
-            step_bytes += gemv_bytes(M, N, K) + quant_bytes(M, K)
-            prod_bytes += gemv_bytes(M, N, K)
+            # the fused kernel reads fp32 x once and never writes or re-reads int8 Xq
+            step_bytes += linear_bytes(M, N, K) if fused else gemv_bytes(M, N, K) + quant_bytes(M, K)
+            prod_bytes += linear_bytes(M, N, K) if fused else gemv_bytes(M, N, K)
             step_ops += 2 * M * N * K
     n_prod = spec["layers"] * len(shapes)
     prod_us_avg = sum(per_shape_us) / len(shapes)
     detail = []
     for j, (name, N, K) in enumerate(shapes):
-        b = gemv_bytes(M, N, K)
+        b = linear_bytes(M, N, K) if fused else gemv_bytes(M, N, K)
         detail.append({"shape": name, "N": N, "K": K, "us": round(per_shape_us[j], 3),
                        "GB/s": round(b / (per_shape_us[j] * 1e3), 1),
                        "TOPS": round(2 * M * N * K / (per_shape_us[j] * 1e6), 2)})
     return dict(ms_step=ms_step, step_bytes=step_bytes, step_ops=step_ops, prod_bytes=prod_bytes,
                 n_prod=n_prod, prod_us_avg=prod_us_avg, detail=detail, resident=resident, setup_s=setup_s,
-                launch="hipGraph" if graph is not None else "eager")
+                launch="hipGraph" if graph is not None else "eager", fused=fused)
 
 
 # ----------------------------------------------------------- CPU baseline leg
@@ -221,7 +246,7 @@ def run_cpu_baseline(args, spec):
             acc = oracle.ternary_matmul(T, Q, lib)
             oracle.scale_epilogue(acc, g, s, lib)
             N, K = T.shape
-            done_bytes += gemv_bytes(M, N, K) + quant_bytes(M, K)
+            done_bytes += linear_bytes(M, N, K)
             done_ops += 2 * M * N * K
         passes += 1
         el = time.perf_counter() - t0
@@ -290,7 +315,9 @@ def main():
         "config": {"workload": spec["desc"], "M": M, "layers": spec["layers"],
                    "shapes": [f"{n} {N}x{K}" for n, N, K in spec["shapes"]],
                    "resident_packed_bytes": g["resident"], "launch": g["launch"],
-                   "step": "per matrix: bt_quant_act + " + ("bt_ternary_gemm" if spec["prefill"] else "bt_ternary_gemv")},
+                   "step": ("per matrix: bt_ternary_linear (quantizer fused into the decode kernel)" if g["fused"]
+                            else "per matrix: bt_quant_act + " +
+                            ("bt_ternary_gemm" if spec["prefill"] else "bt_ternary_gemv"))},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {"hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4) if not spec["prefill"] else None,

@@ -17,6 +17,7 @@ from .api import (
     PackedWeight,
     act_row_bytes,
     linear,
+    linear_workspace_bytes,
     pack_weights,
     pack_workspace_bytes,
     packed_weight_bytes,
@@ -28,6 +29,6 @@ from .api import (
 
 __all__ = [
     "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_MFMA", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
-    "linear", "pack_weights", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
+    "linear", "linear_workspace_bytes", "pack_weights", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
     "ternary_gemv", "unpack_weights",
 ]

@@ -118,12 +118,28 @@ def ternary_gemm(pw: PackedWeight, q, want_y=True, want_acc=False, out_y=None, o
     return _product("bt_ternary_gemm", pw, q, want_y, want_acc, out_y, out_acc)
 
 
-def linear(X: torch.Tensor, pw: PackedWeight) -> torch.Tensor:
-    """Y = the W1.58A8 layer applied to X [M,K] fp32: quant_act then gemv (M <= 16) or gemm."""
-    q = quant_act(X)
-    M = X.shape[0]
-    if M <= GEMV_MAX_M:
-        Y, _ = ternary_gemv(pw, q)
-    else:
-        Y, _ = ternary_gemm(pw, q)
-    return Y
+def linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().bt_linear_workspace_bytes(M, N, K))
+
+
+def linear(X: torch.Tensor, pw: PackedWeight, want_y=True, want_acc=False, out_y=None, out_acc=None,
+           workspace: torch.Tensor | None = None):
+    """bt_ternary_linear: fp32 X [M,K] in, (Y [M,N] fp32, acc [M,N] int32) out.
+
+    One fused launch for decode-sized M; quantize + GEMV/GEMM otherwise.
+    """
+    _need(X, "X", torch.float32)
+    M, K = X.shape
+    if K != pw.K:
+        raise ValueError(f"X has K = {K}, weights have K = {pw.K}")
+    dev = X.device
+    Y = out_y if out_y is not None else (
+        torch.empty((M, pw.N), dtype=torch.float32, device=dev) if want_y else None)
+    acc = out_acc if out_acc is not None else (
+        torch.empty((M, pw.N), dtype=torch.int32, device=dev) if want_acc else None)
+    ws_bytes = linear_workspace_bytes(M, pw.N, K)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    check(lib().bt_ternary_linear(_ptr(pw.data), _ptr(pw.scale), _ptr(X), M, pw.N, K, _ptr(Y), _ptr(acc),
+                                  _ptr(workspace) if ws_bytes else 0, _stream(dev)))
+    return Y, acc

@@ -162,7 +162,7 @@ bt_status bt_ternary_gemv_algo(const void *Wp, const float *w_scale, const int8_
     if (M == 0 || N == 0)
         return ok();
     if (algo == BT_GEMV_AUTO)
-        algo = (M <= 2) ? BT_GEMV_DOT4 : BT_GEMV_MFMA;
+        algo = BT_GEMV_MFMA;
     if (algo == BT_GEMV_DOT4 && M > 4)
         return fail(BT_ERR_UNSUPPORTED, "dot4 gemv takes M <= 4 (got %lld)", (long long)M);
     const int64_t ldq = bt_act_row_bytes(K);
@@ -191,6 +191,56 @@ bt_status bt_ternary_gemm(const void *Wp, const float *w_scale, const int8_t *Xq
     return hip_status(bt::launch_gemm(static_cast<const uint4 *>(Wp), w_scale, Xq, ldq, x_scale, x_sum, M, N, K, Y,
                                       acc, static_cast<hipStream_t>(stream)),
                       "bt_ternary_gemm launch");
+}
+
+// Largest LDS footprint the fused decode kernel is launched with.
+static const size_t kFusedLdsLimit = 64 * 1024;
+
+static bool linear_fused(int64_t M, int64_t N, int64_t K)
+{
+    return M <= BT_GEMV_MAX_M && bt::decode_fused_lds_bytes(M, N, K) <= kFusedLdsLimit;
+}
+
+size_t bt_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K < 0 || linear_fused(M, N, K))
+        return 0;
+    return (size_t)(bt::round_up(M * bt_act_row_bytes(K), 256) + 2 * bt::round_up(4 * M, 256));
+}
+
+bt_status bt_ternary_linear(const void *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+                            float *Y, int32_t *acc, void *workspace, void *stream)
+{
+    if (M < 0 || N < 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30)
+        return fail(BT_ERR_SHAPE, "shape M = %lld, N = %lld out of range", (long long)M, (long long)N);
+    if (bt_status s = check_k(K))
+        return s;
+    if (!Y && !acc)
+        return fail(BT_ERR_NULL, "Y and acc are both NULL");
+    if (M == 0 || N == 0)
+        return ok();
+    if (!w_scale || (K > 0 && (!Wp || !X)))
+        return fail(BT_ERR_NULL, "NULL input pointer");
+    if ((Wp && !aligned(Wp, 16)) || (X && !aligned(X, 4)) || !aligned(w_scale, 4) || (Y && !aligned(Y, 4)) ||
+        (acc && !aligned(acc, 4)))
+        return fail(BT_ERR_ALIGN, "Wp must be 16-byte aligned; X, w_scale, Y and acc 4-byte aligned");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (linear_fused(M, N, K))
+        return hip_status(bt::launch_linear_decode(static_cast<const uint4 *>(Wp), w_scale, X, M, N, K, Y, acc, s),
+                          "bt_ternary_linear launch");
+    if (!workspace)
+        return fail(BT_ERR_NULL, "workspace is NULL but bt_linear_workspace_bytes(%lld, %lld, %lld) = %zu",
+                    (long long)M, (long long)N, (long long)K, bt_linear_workspace_bytes(M, N, K));
+    if (!aligned(workspace, 256))
+        return fail(BT_ERR_ALIGN, "workspace must be 256-byte aligned");
+    int8_t *Xq = static_cast<int8_t *>(workspace);
+    float *sx = reinterpret_cast<float *>(Xq + bt::round_up(M * bt_act_row_bytes(K), 256));
+    int32_t *xsum = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(sx) + bt::round_up(4 * M, 256));
+    if (bt_status st = bt_quant_act(X, M, K, Xq, sx, xsum, stream))
+        return st;
+    if (M <= BT_GEMV_MAX_M)
+        return bt_ternary_gemv_algo(Wp, w_scale, Xq, sx, xsum, M, N, K, Y, acc, BT_GEMV_MFMA, stream);
+    return bt_ternary_gemm(Wp, w_scale, Xq, sx, xsum, M, N, K, Y, acc, stream);
 }
 
 const char *bt_status_str(bt_status s)

@@ -1,0 +1,529 @@
+// Decode product on int8 MFMA for 1 <= M <= 16 tokens, optionally with the per-token
+// activation quantizer fused in (fp32 x in, fp32 y out: one launch per linear layer).
+//
+// "bit-floor" page, "The core math": integer inner loop, one scale multiply at the
+// end; "BitCompute" page, "Features": ternary weights make the product add /
+// subtract / skip; BitNet GPU guide, "Key Components and Source Code Architecture":
+// decode is the memory-bound phase. At decode sizes a launch is dominated by fixed
+// latency (dispatch, one HBM round trip, reductions), so both kernels put every
+// memory request of a wave in flight first and keep the dependent chain short.
+//
+// Work split. A workgroup owns RB 16-row weight blocks (RB = 1, 2 or 4, picked so
+// that small matrices still spread over the 256 CUs) and all of K. A "step" is 256 k:
+// lane group g = lane / 16 takes the 64-k chunk 4*step + g and lane row r = lane % 16,
+// so one step of one block is 64 lanes x 16 bytes. Waves take steps round-robin and
+// load U of them per register batch (U * RB <= 8 uint4 per lane), one batch ahead.
+//
+// MFMA mapping (v_mfma_i32_16x16x64_i8, D = A * B): A = weights, 16 rows x 64 k;
+// B = tokens, 64 k x 16 columns (tokens m >= M are zero). For mask s the A dword j
+// of a lane is (word j & mask s): its byte e is the code of k = 64c + 16j + 4s + e
+// times 4^s (times 16 for s = 3). The matching B dword is bytes 16j + 4s .. +3 of
+// the lane's 64 activation bytes. Three accumulators (weights 1, 4, 16) recombine
+// exactly as a1 + (a4 >> 2) + (a16 >> 4); the code offset (+1) is removed by
+// subtracting sum_k q. The output lane holds D[4g + v][r]: weight row 4g + v of the
+// block, token r.
+//
+// Fused quantization (k_linear_decode). BitNet GPU guide, "Understanding the
+// Two-Phase Architecture": activations are quantized to INT8 with their own scale
+// before the INT8 x INT2 product. Each workgroup loads the fp32 tokens into
+// registers first (they are small and L2-resident), then issues its weight loads,
+// so the quantizer only waits for the activations. It uses the arithmetic of
+// bt_quant_act (a = max |x|, inv = 127.0f / a, q = clamp(rint(x * inv), -127, 127),
+// s_x = a / 127.0f) and stages the int8 tokens in LDS (row pitch Kp + 16 bytes, so
+// the 16-byte operand reads of 16 tokens hit distinct banks).
+#include "bt_internal.h"
+#include "wave.h"
+
+namespace bt {
+namespace {
+
+constexpr int kMaxM = 16;
+constexpr int kPitchPad = 16;
+constexpr int kXRegs = 16;     // float4 of fp32 activations a thread keeps in registers
+constexpr int kFusedWaves = 8;
+constexpr int kDirectWaves = 4;
+
+__host__ __device__ constexpr int batch_steps(int rb) { return 8 / rb; }
+
+// Four MFMAs of one step for each of the RB row blocks.
+template <int RB>
+__device__ inline void mfma_step(const uint4 (&w)[RB], const int32_t (&xw)[16], v4i (&a1)[RB], v4i (&a4)[RB],
+                                 v4i (&a16)[RB])
+{
+    const v4i b0 = {xw[0], xw[4], xw[8], xw[12]};
+    const v4i b1 = {xw[1], xw[5], xw[9], xw[13]};
+    const v4i b2 = {xw[2], xw[6], xw[10], xw[14]};
+    const v4i b3 = {xw[3], xw[7], xw[11], xw[15]};
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+        const uint32_t pw[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+        v4i s0, s1, s2, s3;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s0[j] = (int)(pw[j] & kMask0);
+            s1[j] = (int)(pw[j] & kMask1);
+            s2[j] = (int)(pw[j] & kMask2);
+            s3[j] = (int)((pw[j] >> 2) & kMask2);
+        }
+        a1[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(s0, b0, a1[k], 0, 0, 0);
+        a4[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(s1, b1, a4[k], 0, 0, 0);
+        a16[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(s2, b2, a16[k], 0, 0, 0);
+        a16[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(s3, b3, a16[k], 0, 0, 0);
+    }
+}
+
+// Weight uint4 of block b16, chunk c, lane row r (padding words outside the matrix).
+__device__ inline uint4 load_w(const uint4 *__restrict__ Wp, int b16, int NB16, int c, int KC, int r, bool ok)
+{
+    return (ok && b16 < NB16) ? Wp[((int64_t)(b16 >> 2) * KC + c) * 64 + 16 * (b16 & 3) + r]
+                              : make_uint4(kPadWord, kPadWord, kPadWord, kPadWord);
+}
+
+__device__ inline void unpack16(const uint4 (&v)[4], int32_t (&xw)[16])
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        xw[4 * q + 0] = (int32_t)v[q].x;
+        xw[4 * q + 1] = (int32_t)v[q].y;
+        xw[4 * q + 2] = (int32_t)v[q].z;
+        xw[4 * q + 3] = (int32_t)v[q].w;
+    }
+}
+
+// Partial accumulators of all waves -> y and acc. red[w][k][v][lane]; o = m * rows + nl.
+// token_stats(m, qs, sx) supplies sum_k q and s_x of token m.
+template <int WAVES, int RB, typename Stats>
+__device__ inline void epilogue(const int *red, int tid, int M, int64_t N, float gamma, Stats token_stats,
+                                float *__restrict__ Y, int32_t *__restrict__ ACC)
+{
+    constexpr int rows = 16 * RB;
+    for (int o = tid; o < M * rows; o += WAVES * 64) {
+        const int m = o / rows;
+        const int nl = o - m * rows;
+        const int64_t n = (int64_t)blockIdx.x * rows + nl;
+        if (n >= N)
+            continue;
+        const int k = nl >> 4, gg = (nl >> 2) & 3, v = nl & 3;
+        const int src = gg * 16 + m;
+        int s = 0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w)
+            s += red[((w * RB + k) * 4 + v) * 64 + src];
+        int qs;
+        float sxm;
+        token_stats(m, qs, sxm);
+        const int acc = s - qs;
+        if (ACC)
+            ACC[(int64_t)m * N + n] = acc;
+        if (Y)
+            Y[(int64_t)m * N + n] = (float)acc * (gamma * sxm);
+    }
+}
+
+// ------------------------------------------------------------ direct kernel
+// Pre-quantized int8 activations read straight from global memory (L2) per step.
+template <int RB>
+__global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct(
+    const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
+    const float *__restrict__ sx_in, const int32_t *__restrict__ xsum_in, int M, int64_t N, int KC, int NB16,
+    float *__restrict__ Y, int32_t *__restrict__ ACC)
+{
+    constexpr int WAVES = kDirectWaves;
+    constexpr int U = 2;
+    __shared__ int red[WAVES * RB * 256];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int g = lane >> 4;
+    const int r = lane & 15;
+    const int nsteps = (KC + 3) >> 2;
+    const int nmine = (wave < nsteps) ? (nsteps - 1 - wave) / WAVES + 1 : 0;
+
+    v4i a1[RB], a4[RB], a16[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k)
+        a1[k] = a4[k] = a16[k] = v4i{0, 0, 0, 0};
+
+    for (int i0 = 0; i0 < nmine; i0 += U) {
+        uint4 w[U][RB];
+        uint4 xv[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u;
+            const int c = 4 * (wave + WAVES * i) + g;
+            const bool ok = (i < nmine) && (c < KC);
+#pragma unroll
+            for (int k = 0; k < RB; ++k)
+                w[u][k] = load_w(Wp, blockIdx.x * RB + k, NB16, c, KC, r, ok);
+            const uint4 *p = reinterpret_cast<const uint4 *>(Xq + (int64_t)r * ldq + (int64_t)c * 64);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xv[u][q] = (ok && r < M) ? p[q] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (i0 + u >= nmine)
+                break;
+            int32_t xw[16];
+            unpack16(xv[u], xw);
+            mfma_step<RB>(w[u], xw, a1, a4, a16);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < RB; ++k)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            red[((wave * RB + k) * 4 + v) * 64 + lane] = a1[k][v] + (a4[k][v] >> 2) + (a16[k][v] >> 4);
+    __syncthreads();
+    epilogue<WAVES, RB>(red, tid, M, N, w_scale[0],
+                        [&](int m, int &qs, float &sxm) {
+                            qs = xsum_in[m];
+                            sxm = sx_in[m];
+                        },
+                        Y, ACC);
+}
+
+// ------------------------------------------------------------- fused kernel
+// Eight waves per workgroup. Wave w owns the 16-row block blockIdx.x * (8/S) + w / S
+// and the k-split w % S of it: steps st = w % S, w % S + S, ... For S = 1 a wave owns
+// all of K and its epilogue runs straight from its MFMA registers; for S > 1 the S
+// partial sums of a block are added through LDS. MT = compile-time token capacity
+// (M <= MT); RPT float4 of each token per thread stay in registers for the quantizer.
+template <int MT, int S, bool VEC>
+__global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
+    const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const float *__restrict__ X, int M, int64_t N,
+    int K, int KC, int NB16, float *__restrict__ Y, int32_t *__restrict__ ACC)
+{
+    constexpr int WAVES = kFusedWaves;
+    constexpr int T = WAVES * 64;
+    constexpr int U = 4;              // steps per register batch
+    constexpr int RPT = kXRegs / MT;
+    constexpr int RBW = WAVES / S;    // row blocks per workgroup
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    float *s_apart = reinterpret_cast<float *>(smem);                  // [WAVES][kMaxM]
+    int *s_qpart = reinterpret_cast<int *>(s_apart + WAVES * kMaxM);   // [WAVES][kMaxM]
+    int *red = s_qpart + WAVES * kMaxM;                                // [WAVES][4][64] (S > 1)
+    int8_t *xq = reinterpret_cast<int8_t *>(red + (S > 1 ? WAVES * 256 : 0));
+    const int pitch = KC * 64 + kPitchPad;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int g = lane >> 4;
+    const int r = lane & 15;
+    const int ks = wave % S;
+    const int b16 = blockIdx.x * RBW + wave / S;
+    const int nsteps = (KC + 3) >> 2;
+    const int nmine = (ks < nsteps) ? (nsteps - 1 - ks) / S + 1 : 0;
+    const int nb = (nmine + U - 1) / U;
+
+    const int K4 = (K + 3) >> 2;
+    const int R = (K4 + T - 1) / T;
+    const bool regpath = VEC && R <= RPT;
+
+    auto load4 = [&](const float *xr, int k4) -> float4 {
+        if (VEC)
+            return reinterpret_cast<const float4 *>(xr)[k4];
+        const int k = 4 * k4;
+        return make_float4(xr[k], (k + 1 < K) ? xr[k + 1] : 0.0f, (k + 2 < K) ? xr[k + 2] : 0.0f,
+                           (k + 3 < K) ? xr[k + 3] : 0.0f);
+    };
+
+    // 1. Activations first (waiting for them then does not wait for the weights). Each
+    //    slot is one load at a clamped, always valid address and a select.
+    float4 xr[MT][RPT];
+    if (regpath) {
+        const float4 *X4 = reinterpret_cast<const float4 *>(X);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                xr[m][i] = make_float4(0, 0, 0, 0);
+                if (m < M && i < R) {  // uniform
+                    const int k4 = tid + i * T;
+                    const float4 v = X4[(int64_t)m * K4 + min(k4, K4 - 1)];
+                    xr[m][i] = (k4 < K4) ? v : make_float4(0, 0, 0, 0);
+                }
+            }
+    }
+
+    // 2. The wave's first weight batch.
+    uint4 wa[U], wb[U];
+    auto load_batch = [&](uint4 (&w)[U], int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = b * U + u;
+            const int c = 4 * (ks + S * i) + g;
+            w[u] = load_w(Wp, b16, NB16, c, KC, r, (i < nmine) && (c < KC));
+        }
+    };
+    if (nb > 0)
+        load_batch(wa, 0);
+    if (nb > 1)
+        load_batch(wb, 1);
+
+    // 3. Per-token absmax: wave partials in LDS.
+    if (regpath) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m < M) {  // a guard, not a break: the loop must stay fully unrolled
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < RPT; ++i)
+                    a = fmaxf(a, fmaxf(fmaxf(fabsf(xr[m][i].x), fabsf(xr[m][i].y)),
+                                       fmaxf(fabsf(xr[m][i].z), fabsf(xr[m][i].w))));
+                a = wave_max_f32(a);
+                if (lane == 0)
+                    s_apart[wave * kMaxM + m] = a;
+            }
+        }
+    } else {
+        for (int m = 0; m < M; ++m) {
+            const float *xm = X + (int64_t)m * K;
+            float a = 0.0f;
+#pragma unroll 4
+            for (int k4 = tid; k4 < K4; k4 += T) {
+                const float4 v = load4(xm, k4);
+                a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+            a = wave_max_f32(a);
+            if (lane == 0)
+                s_apart[wave * kMaxM + m] = a;
+        }
+    }
+    __syncthreads();
+
+    // 4. Quantize into LDS; per-wave partial sums of q.
+    auto token_amax = [&](int m) {
+        float amax = s_apart[m];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w)
+            amax = fmaxf(amax, s_apart[w * kMaxM + m]);
+        return amax;
+    };
+    if (regpath) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m < M) {
+                const float amax = token_amax(m);
+                const float inv = (amax == 0.0f) ? 0.0f : 127.0f / amax;
+                int8_t *qrow = xq + m * pitch;
+                int sum = 0;
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    const int k4 = tid + i * T;
+                    if (k4 < KC * 16) {
+                        const uint32_t p = (k4 < K4) ? quant_pack4(xr[m][i], inv) : 0u;
+                        sum += sum_bytes_s8(p);
+                        *reinterpret_cast<uint32_t *>(qrow + 4 * k4) = p;
+                    }
+                }
+                // zero padding past the register-held part of the row
+                for (int k4 = tid + RPT * T; k4 < KC * 16; k4 += T)
+                    *reinterpret_cast<uint32_t *>(qrow + 4 * k4) = 0u;
+                sum = wave_sum_i32(sum);
+                if (lane == 0)
+                    s_qpart[wave * kMaxM + m] = sum;
+            }
+        }
+    } else {
+        for (int m = 0; m < M; ++m) {
+            const float amax = token_amax(m);
+            const float inv = (amax == 0.0f) ? 0.0f : 127.0f / amax;
+            int8_t *qrow = xq + m * pitch;
+            const float *xm = X + (int64_t)m * K;
+            int sum = 0;
+            for (int k4 = tid; k4 < KC * 16; k4 += T) {
+                const uint32_t p = (k4 < K4) ? quant_pack4(load4(xm, k4), inv) : 0u;
+                sum += sum_bytes_s8(p);
+                *reinterpret_cast<uint32_t *>(qrow + 4 * k4) = p;
+            }
+            sum = wave_sum_i32(sum);
+            if (lane == 0)
+                s_qpart[wave * kMaxM + m] = sum;
+        }
+    }
+    __syncthreads();
+
+    // 5. Stream the wave's weights, two batches in flight, MFMAs on the older one.
+    v4i a1[1], a4[1], a16[1];
+    a1[0] = a4[0] = a16[0] = v4i{0, 0, 0, 0};
+    auto compute_batch = [&](const uint4 (&w)[U], int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = b * U + u;
+            if (i < nmine) {
+                const int c = 4 * (ks + S * i) + g;
+                uint4 xv[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                               make_uint4(0, 0, 0, 0)};
+                if (r < M && c < KC) {
+                    const uint4 *p = reinterpret_cast<const uint4 *>(xq + r * pitch + c * 64);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        xv[q] = p[q];
+                }
+                int32_t xw[16];
+                unpack16(xv, xw);
+                const uint4 wk[1] = {w[u]};
+                mfma_step<1>(wk, xw, a1, a4, a16);
+            }
+        }
+    };
+    for (int b = 0; b < nb; b += 2) {
+        compute_batch(wa, b);
+        if (b + 2 < nb)
+            load_batch(wa, b + 2);
+        if (b + 1 < nb) {
+            compute_batch(wb, b + 1);
+            if (b + 3 < nb)
+                load_batch(wb, b + 3);
+        }
+    }
+
+    // 6. Combine the k-splits of each block (S > 1) and write y / acc. Lane (g, r) holds
+    //    rows 4g + v of its block for token r.
+    int part[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        part[v] = a1[0][v] + (a4[0][v] >> 2) + (a16[0][v] >> 4);
+    if (S > 1) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            red[(wave * 4 + v) * 64 + lane] = part[v];
+        __syncthreads();
+        if (ks == 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                int sum = part[v];
+#pragma unroll
+                for (int j = 1; j < S; ++j)
+                    sum += red[((wave + j) * 4 + v) * 64 + lane];
+                part[v] = sum;
+            }
+        }
+    }
+    if (ks == 0 && r < M) {
+        float amax = s_apart[r];
+        int qs = s_qpart[r];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+            amax = fmaxf(amax, s_apart[w * kMaxM + r]);
+            qs += s_qpart[w * kMaxM + r];
+        }
+        const float scale = w_scale[0] * ((amax == 0.0f) ? 0.0f : amax / 127.0f);
+        const int64_t n0 = (int64_t)b16 * 16 + 4 * g;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t n = n0 + v;
+            if (n < N) {
+                const int acc = part[v] - qs;
+                if (ACC)
+                    ACC[(int64_t)r * N + n] = acc;
+                if (Y)
+                    Y[(int64_t)r * N + n] = (float)acc * scale;
+            }
+        }
+    }
+}
+
+int pick_rb(int64_t N)
+{
+    const int64_t nb16 = (N + 15) / 16;
+    if (nb16 / 4 >= 256)
+        return 4;
+    if (nb16 / 2 >= 256)
+        return 2;
+    return 1;
+}
+
+int pick_mt(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+
+// k-splits per 16-row block: enough waves to give every SIMD one (1024 waves).
+int pick_s(int64_t N)
+{
+    const int64_t nb16 = (N + 15) / 16;
+    int s = 1;
+    while (s < 8 && nb16 * s < 1024)
+        s *= 2;
+    return s;
+}
+
+size_t fused_lds(int64_t M, int64_t K, int s)
+{
+    const int64_t KC = (K + 63) / 64;
+    return 2 * kFusedWaves * kMaxM * 4 + (s > 1 ? kFusedWaves * 256 * 4 : 0) + (size_t)M * (KC * 64 + kPitchPad);
+}
+
+template <int MT, int S>
+hipError_t launch_fused_t(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+                          float *Y, int32_t *acc, hipStream_t s)
+{
+    constexpr int RBW = kFusedWaves / S;
+    const int KC = (int)((K + 63) / 64);
+    const int NB16 = (int)(((N + 63) / 64) * 4);
+    const int64_t nb16 = (N + 15) / 16;
+    const dim3 grid((unsigned)((nb16 + RBW - 1) / RBW)), block(kFusedWaves * 64);
+    const size_t lds = fused_lds(M, K, S);
+    const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    if (vec)
+        hipLaunchKernelGGL((k_linear_decode<MT, S, true>), grid, block, lds, s, Wp, w_scale, X, (int)M, N, (int)K,
+                           KC, NB16, Y, acc);
+    else
+        hipLaunchKernelGGL((k_linear_decode<MT, S, false>), grid, block, lds, s, Wp, w_scale, X, (int)M, N,
+                           (int)K, KC, NB16, Y, acc);
+    return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_fused_mt(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+                           float *Y, int32_t *acc, hipStream_t s)
+{
+    switch (pick_s(N)) {
+    case 1: return launch_fused_t<MT, 1>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    case 2: return launch_fused_t<MT, 2>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    case 4: return launch_fused_t<MT, 4>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    default: return launch_fused_t<MT, 8>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    }
+}
+
+template <int RB>
+hipError_t launch_direct_t(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
+                           const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                           hipStream_t s)
+{
+    const int KC = (int)((K + 63) / 64);
+    const int NB16 = (int)(((N + 63) / 64) * 4);
+    const int64_t nb16 = (N + 15) / 16;
+    hipLaunchKernelGGL((k_gemv_direct<RB>), dim3((unsigned)((nb16 + RB - 1) / RB)), dim3(kDirectWaves * 64), 0, s,
+                       Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, NB16, Y, acc);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K) { return fused_lds(M, K, pick_s(N)); }
+
+hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq,
+                            const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
+                            int32_t *acc, hipStream_t s)
+{
+    switch (pick_rb(N)) {
+    case 4: return launch_direct_t<4>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    case 2: return launch_direct_t<2>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    default: return launch_direct_t<1>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    }
+}
+
+hipError_t launch_linear_decode(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N,
+                                int64_t K, float *Y, int32_t *acc, hipStream_t s)
+{
+    switch (pick_mt(M)) {
+    case 1: return launch_fused_mt<1>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    case 2: return launch_fused_mt<2>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    case 4: return launch_fused_mt<4>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    case 8: return launch_fused_mt<8>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    default: return launch_fused_mt<16>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    }
+}
+
+}  // namespace bt

@@ -1,0 +1,72 @@
+// Wave64 reductions on gfx950 without LDS traffic: DPP within each 16-lane row
+// (quad swaps, half-row mirror, row mirror), then v_permlane16_swap and
+// v_permlane32_swap to combine the four rows. Every lane ends with the result.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bt {
+
+template <int CTRL>
+__device__ inline int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <typename Op>
+__device__ inline uint32_t wave_reduce_bits(uint32_t v, Op op)
+{
+    v = op(v, (uint32_t)dpp_i<kDppQuadXor1>((int)v));
+    v = op(v, (uint32_t)dpp_i<kDppQuadXor2>((int)v));
+    v = op(v, (uint32_t)dpp_i<kDppRowHalfMirror>((int)v));
+    v = op(v, (uint32_t)dpp_i<kDppRowMirror>((int)v));
+    // Each lane of a row sees its own row in one output of the swap and the partner
+    // row in the other, so a symmetric op of the pair reduces across the pair of rows.
+    auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op((uint32_t)p16[0], (uint32_t)p16[1]);
+    auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = op((uint32_t)p32[0], (uint32_t)p32[1]);
+    return v;
+}
+
+__device__ inline float wave_max_f32(float v)
+{
+    return __uint_as_float(wave_reduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+
+__device__ inline int wave_sum_i32(int v)
+{
+    return (int)wave_reduce_bits((uint32_t)v, [](uint32_t a, uint32_t b) { return (uint32_t)((int)a + (int)b); });
+}
+
+// Per-token int8 quantization of one value (the rule of bt_quant_act).
+__device__ inline int quant_one(float x, float inv)
+{
+    float r = rintf(x * inv);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+__device__ inline uint32_t quant_pack4(float4 v, float inv)
+{
+    const int e0 = quant_one(v.x, inv), e1 = quant_one(v.y, inv), e2 = quant_one(v.z, inv),
+              e3 = quant_one(v.w, inv);
+    return (uint32_t)(e0 & 0xff) | ((uint32_t)(e1 & 0xff) << 8) | ((uint32_t)(e2 & 0xff) << 16) |
+           ((uint32_t)(e3 & 0xff) << 24);
+}
+
+__device__ inline int sum_bytes_s8(uint32_t p)
+{
+    return (int)(int8_t)(p & 0xff) + (int)(int8_t)((p >> 8) & 0xff) + (int)(int8_t)((p >> 16) & 0xff) +
+           (int)(int8_t)(p >> 24);
+}
+
+}  // namespace bt

@@ -156,6 +156,29 @@ bt_status bt_ternary_gemm(const void *Wp, const float *w_scale, const int8_t *Xq
                           const float *x_scale, const int32_t *x_sum, int64_t M, int64_t N,
                           int64_t K, float *Y, int32_t *acc, void *stream);
 
+/*
+ * bt_ternary_linear -- the whole per-call path of the layer in one entry point:
+ * fp32 activations in, fp32 outputs out (per-token absmax int8 quantization, the
+ * integer ternary product and the scale epilogue). Follows the BitNet GPU guide,
+ * "Understanding the Two-Phase Architecture" (the kernel-backed linear layer
+ * quantizes its inputs to INT8 and calls the INT8 x INT2 product) and "Key
+ * Components and Source Code Architecture" (decode is memory-bound: one launch per
+ * layer keeps the per-call latency down).
+ *   X          [M,K] fp32 row-major, 4-byte aligned.
+ *   Y, acc     as for bt_ternary_gemv (either may be NULL, not both).
+ *   workspace  bt_linear_workspace_bytes(M,N,K) bytes of device scratch, 256-byte
+ *              aligned, or NULL when that size is 0.
+ * For M <= BT_GEMV_MAX_M and M * (K rounded up to 64) small enough for LDS the
+ * quantizer runs inside the decode kernel (one launch, no workspace); otherwise the
+ * call runs bt_quant_act into the workspace, then bt_ternary_gemv or
+ * bt_ternary_gemm. Both routes give results bit-identical to calling bt_quant_act
+ * and bt_ternary_gemv / bt_ternary_gemm yourself.
+ */
+size_t bt_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+bt_status bt_ternary_linear(const void *Wp, const float *w_scale, const float *X, int64_t M,
+                            int64_t N, int64_t K, float *Y, int32_t *acc, void *workspace,
+                            void *stream);
+
 /* Static text for a status code. */
 const char *bt_status_str(bt_status s);
 

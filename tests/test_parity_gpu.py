@@ -346,3 +346,73 @@ def test_side_stream_and_graph_replay():
         eager_Y, eager_acc = bt.ternary_gemv(pw, bt.quant_act(to_dev(X)), want_acc=True)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(Y.cpu().numpy(), eager_Y.cpu().numpy())
+
+
+# ------------------------------------------------- fused linear entry point
+LINEAR_CASES = [(1, 1, 1), (1, 100, 300), (2, 130, 129), (3, 65, 1000), (5, 200, 700), (8, 64, 64),
+                (16, 300, 517), (16, 1000, 2560), (1, 2560, 6912), (8, 4096, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_CASES)
+def test_linear_fused(M, N, K):
+    """bt_ternary_linear (quantizer fused into the decode kernel) against the oracle, and bit-identical
+    to the split route bt_quant_act + bt_ternary_gemv."""
+    note(f"linear M={M} N={N} K={K}")
+    assert bt.linear_workspace_bytes(M, N, K) == 0  # these shapes take the fused kernel
+    W = synth.gaussian((N, K), 9200 + N + K, 0.02)
+    X = synth.gaussian((M, K), 9700 + M + K)
+    if M >= 3:
+        X[1] = 0.0
+    ref = oracle_layer(W, X)
+    pw = gpu_pack(W)
+    Y, acc = bt.linear(to_dev(X), pw, want_acc=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    assert tol_ok(Y.cpu().numpy(), ref["Y"])
+    Ys, _ = bt.ternary_gemv(pw, gpu_quant(X), algo=bt.GEMV_MFMA)
+    np.testing.assert_array_equal(Y.cpu().numpy(), Ys.cpu().numpy())
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 512, 8192), (16, 600, 28672), (40, 300, 700), (300, 257, 1000)])
+def test_linear_workspace_routes(M, N, K):
+    """Shapes past the fused kernel's LDS budget (and M > 16) go through the workspace route."""
+    note(f"linear route M={M} N={N} K={K}")
+    assert bt.linear_workspace_bytes(M, N, K) > 0
+    W = synth.gaussian((N, K), 9300 + N, 0.02)
+    X = synth.gaussian((M, K), 9800 + M)
+    ref = oracle_layer(W, X)
+    Y, acc = bt.linear(to_dev(X), gpu_pack(W), want_acc=True)
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    assert tol_ok(Y.cpu().numpy(), ref["Y"])
+
+
+@pytest.mark.parametrize("j,name,N,K", [(j, *s) for j, s in enumerate(synth.SHAPES_2B)])
+def test_linear_2b_decode_full(j, name, N, K):
+    """The benchmark's call: fused bt_ternary_linear at M=1 on the 2B decode shapes, every output."""
+    note(f"linear 2B {name}")
+    W = synth.layer_weight(synth.CFG_2B_DECODE, 1, j, N, K)
+    X = synth.layer_activation(synth.CFG_2B_DECODE, j, 1, K)
+    ref = oracle_layer(W, X)
+    Y, acc = bt.linear(to_dev(X), gpu_pack(W), want_acc=True)
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    assert tol_ok(Y.cpu().numpy(), ref["Y"])
+
+
+def test_linear_100b_gate_up_m1_sampled():
+    """Largest decode matrix (57344 x 8192, 117 MB packed) through the fused call, sampled rows."""
+    note("linear 100B gate_up")
+    j = 2
+    name, N, K = synth.SHAPES_100B[j]
+    W = synth.layer_weight(synth.CFG_100B_DECODE, 0, j, N, K)
+    X = synth.layer_activation(synth.CFG_100B_DECODE, j, 1, K)
+    g = oracle.absmean(W)
+    rows = np.arange(0, N, 13)
+    T = oracle.ternarize(W[rows], g)
+    Q, s, qs = oracle.quant_act(X)
+    acc_ref = oracle.ternary_matmul(T, Q)
+    pw = gpu_pack(W)
+    del W
+    assert f32_bits(pw.scale.cpu().numpy()[0]) == f32_bits(g)
+    Y, acc = bt.linear(to_dev(X), pw, want_acc=True)
+    np.testing.assert_array_equal(acc.cpu().numpy()[:, rows], acc_ref)
+    assert tol_ok(Y.cpu().numpy()[:, rows], oracle.scale_epilogue(acc_ref, g, s))
