@@ -1,6 +1,7 @@
 """Benchmark of the W1.58A8 ternary linear layer hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--m M] [--split] [--eager]
+                    [--no-cpu-baseline]
 
 A step is one pass of the whole per-call hot path over one batch of synthetic input:
 for every resident weight matrix, quantize its fp32 activations per token to int8, run
@@ -8,7 +9,8 @@ the integer ternary product and apply the scale epilogue -- one bt_ternary_linea
 per matrix (a single fused kernel at decode sizes; bt_quant_act + bt_ternary_gemm for
 prefill). ``--split`` times the unfused route (bt_quant_act + bt_ternary_gemv/gemm as
 two launches) instead. Weight packing is offline and outside the timed region. Inputs
-are resident in HBM before timing starts. Prints ONE JSON line (one GPU).
+are resident in HBM before timing starts; the step is replayed as one HIP graph.
+Prints ONE JSON line.
 
 Workloads (``--workload``):
   2b_decode   (default) 2B-class decode, M = 1: 30 layers x {QKV 3840x2560, O 2560x2560,
@@ -19,24 +21,37 @@ Workloads (``--workload``):
   100b_decode 100B-class single-layer sweep at --m (1, 16): 3 independently seeded copies
               of {10240x8192, 8192x8192, 57344x8192, 8192x28672} (642 MB) -> GB/s.
   2b_prefill  2B-class prefill at --m (256, 2048): the 2B layer shapes, 30 layers -> TOPS.
+
+The dominant kernel's average duration comes from a second graph holding only the
+product launches of one step (for the fused decode route that is the whole step),
+timed with HIP events on the stream it runs on. HBM traffic per launch comes from a
+committed rocprofv3 counter summary under profiles/ (see ``--summarize-pmc``) and is
+reported only while the kernel sources still hash to the values recorded there.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
-import math
 import os
 import sys
 import time
-
-import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "ternary GEMV HBM GB/s (% of peak) at 2B decode shapes; prefill GEMM int8 TOPS"
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+HBM_PEAK_GBS = 8000.0    # MI355X HBM3E, 8 TB/s
 INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
+CSRC = os.path.join(ROOT, "bit_ternary_weight_absmean_amd", "csrc")
+# Sources each dominant kernel is built from (their hash tags a traffic summary).
+KERNEL_SOURCES = {
+    "k_linear_decode": ["decode.hip", "wave.h", "bt_internal.h"],
+    "k_gemv_direct": ["decode.hip", "bt_internal.h"],
+    "k_gemm": ["gemm.hip", "bt_internal.h"],
+}
 
 
 def parse():
@@ -46,12 +61,17 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="2b_decode", choices=["2b_decode", "7b_decode", "100b_decode", "2b_prefill"])
     p.add_argument("--m", type=int, default=None, help="tokens per call (default: 1 for decode, 2048 for prefill)")
-    p.add_argument("--eager", action="store_true", help="launch kernels one by one instead of replaying a graph")
+    p.add_argument("--eager", action="store_true", help="launch kernels one by one instead of replaying graphs")
     p.add_argument("--split", action="store_true", help="time bt_quant_act + product as two launches per matrix")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain 1 GiB device copy 10 times (HBM counter calibration)")
+    p.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR",
+                                                        "OUT_JSON"),
+                   help="write a traffic summary from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs of this "
+                        "workload and of --calib-copy, for the workload's dominant kernel")
+    p.add_argument("--command", default="", help="the rocprofv3 command line recorded with --summarize-pmc")
     return p.parse_args()
 
 
@@ -60,33 +80,45 @@ def workload_spec(name, m):
     from bit_ternary_weight_absmean_amd import synth
 
     if name == "2b_decode":
-        return dict(cfg=synth.CFG_2B_DECODE, shapes=synth.SHAPES_2B, layers=30, M=m or 1, prefill=False,
-                    desc="2B-class decode GEMVs, 30 layers resident")
+        return dict(name=name, cfg=synth.CFG_2B_DECODE, shapes=synth.SHAPES_2B, layers=30, M=m or 1,
+                    prefill=False, desc="2B-class decode GEMVs, 30 layers resident")
     if name == "7b_decode":
-        return dict(cfg=synth.CFG_7B_DECODE, shapes=synth.SHAPES_7B, layers=32, M=m or 1, prefill=False,
-                    desc="7B-class decode GEMVs, 32 layers resident")
+        return dict(name=name, cfg=synth.CFG_7B_DECODE, shapes=synth.SHAPES_7B, layers=32, M=m or 1,
+                    prefill=False, desc="7B-class decode GEMVs, 32 layers resident")
     if name == "100b_decode":
-        return dict(cfg=synth.CFG_100B_DECODE, shapes=synth.SHAPES_100B, layers=3, M=m or 1, prefill=False,
-                    desc="100B-class single-layer decode sweep, 3 seeded copies resident")
-    return dict(cfg=synth.CFG_2B_PREFILL, shapes=synth.SHAPES_2B, layers=30, M=m or 2048, prefill=True,
+        return dict(name=name, cfg=synth.CFG_100B_DECODE, shapes=synth.SHAPES_100B, layers=3, M=m or 1,
+                    prefill=False, desc="100B-class single-layer decode sweep, 3 seeded copies resident")
+    return dict(name=name, cfg=synth.CFG_2B_PREFILL, shapes=synth.SHAPES_2B, layers=30, M=m or 2048, prefill=True,
                 desc="2B-class prefill GEMMs, 30 layers resident")
 
 
 def gemv_bytes(M, N, K):
-    """Algorithmic HBM bytes of one product call: 2-bit weights, int8 activations read,
-    fp32 output written, gamma + s_x + sum q read."""
+    """Algorithmic HBM bytes of one product call on pre-quantized activations: 2-bit
+    weights, int8 activations read, fp32 output written, gamma + s_x + sum q read."""
     return N * K // 4 + M * K + 4 * M * N + 4 + 8 * M
 
 
 def linear_bytes(M, N, K):
-    """Algorithmic HBM bytes of one fused decode call: 2-bit weights and fp32 activations
-    read, fp32 output written, gamma read."""
+    """Algorithmic HBM bytes of one fused call: 2-bit weights and fp32 activations read,
+    fp32 output written, gamma read."""
     return N * K // 4 + 4 * M * K + 4 * M * N + 4
 
 
 def quant_bytes(M, K):
     """Algorithmic bytes of one activation quantization: fp32 read, int8 + s_x + sum q written."""
     return 4 * M * K + M * K + 8 * M
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload, kernel, M):
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_m{M}.json")
 
 
 # ----------------------------------------------------------------- main leg
@@ -129,105 +161,90 @@ def run_gpu(args, spec):
         wss.append(torch.empty(wb, dtype=torch.uint8, device=dev) if wb else None)
     torch.cuda.synchronize()
 
-    product = bt.ternary_gemm if spec["prefill"] else bt.ternary_gemv
-
-    if args.split:
-        def call(j, pw):
-            bt.quant_act(xs[j], out=qs[j])
-            product(pw, qs[j], out_y=ys[j])
+    fused = (not args.split) and all(bt.linear_workspace_bytes(M, N, K) == 0 for _, N, K in shapes)
+    if fused:
+        kernel = "k_linear_decode"
+    elif spec["prefill"] or M > bt.GEMV_MAX_M:
+        kernel = "k_gemm"
     else:
-        def call(j, pw):
-            bt.linear(xs[j], pw, out_y=ys[j], workspace=wss[j])
+        kernel = "k_gemv_direct"
+    product = bt.ternary_gemm if kernel == "k_gemm" else bt.ternary_gemv
 
     def step():
         for row in packed:
             for j, pw in enumerate(row):
-                call(j, pw)
+                if args.split:
+                    bt.quant_act(xs[j], out=qs[j])
+                    product(pw, qs[j], out_y=ys[j])
+                else:
+                    bt.linear(xs[j], pw, out_y=ys[j], workspace=wss[j])
+
+    def products():
+        """Only the dominant kernel's launches of one step (activations already quantized)."""
+        for row in packed:
+            for j, pw in enumerate(row):
+                if fused:
+                    bt.linear(xs[j], pw, out_y=ys[j])
+                else:
+                    product(pw, qs[j], out_y=ys[j])
 
     stream = torch.cuda.Stream(device=dev)
-    graph = None
-    with torch.cuda.stream(stream):
-        for _ in range(2):
-            step()
-        stream.synchronize()
+
+    def timed(fn, steps, warmup):
+        run = fn
         if not args.eager:
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=stream):
-                step()
+                fn()
             stream.synchronize()
-
-        run = graph.replay if graph is not None else step
-        for _ in range(args.warmup):
+            run = graph.replay
+        for _ in range(warmup):
             run()
         stream.synchronize()
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             run()
         end.record(stream)
         end.synchronize()
         torch.cuda.synchronize()
-        ms_step = start.elapsed_time(end) / args.steps
+        return start.elapsed_time(end) / steps
 
-        # Dominant kernel (the product, with the quantizer fused in at decode sizes) timed
-        # live: one event pair around every product launch, eager, on the kernels' stream.
-        per_shape_ms = [0.0] * len(shapes)
-        reps = max(2, min(args.steps, 5))
-        pairs = []
-        fused = not args.split and not spec["prefill"]
-        for _ in range(reps):
-            for row in packed:
-                for j, pw in enumerate(row):
-                    if not fused:
-                        bt.quant_act(xs[j], out=qs[j])
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    if fused:
-                        bt.linear(xs[j], pw, out_y=ys[j], workspace=wss[j])
-                    else:
-                        product(pw, qs[j], out_y=ys[j])
-                    e1.record(stream)
-                    pairs.append((j, e0, e1))
+    with torch.cuda.stream(stream):
+        for _ in range(2):  # eager warmup (library load, first touch)
+            step()
         stream.synchronize()
-    for j, e0, e1 in pairs:
-        per_shape_ms[j] += e0.elapsed_time(e1)
-    n_per_shape = reps * spec["layers"]
-    per_shape_us = [1e3 * t / n_per_shape for t in per_shape_ms]
+        ms_step = timed(step, args.steps, args.warmup)
+        ms_prod = ms_step if fused else timed(products, args.steps, args.warmup)
 
-    step_bytes = 0
-    step_ops = 0
-    prod_bytes = 0
-    fused = not args.split and not spec["prefill"]
+    step_bytes = step_ops = prod_bytes = 0
     for row in packed:
         for j, (_, N, K) in enumerate(shapes):
             # the fused kernel reads fp32 x once and never writes or re-reads int8 Xq
-            step_bytes += linear_bytes(M, N, K) if fused else gemv_bytes(M, N, K) + quant_bytes(M, K)
-            prod_bytes += linear_bytes(M, N, K) if fused else gemv_bytes(M, N, K)
+            if fused:
+                step_bytes += linear_bytes(M, N, K)
+                prod_bytes += linear_bytes(M, N, K)
+            else:
+                step_bytes += gemv_bytes(M, N, K) + quant_bytes(M, K)
+                prod_bytes += gemv_bytes(M, N, K)
             step_ops += 2 * M * N * K
     n_prod = spec["layers"] * len(shapes)
-    prod_us_avg = sum(per_shape_us) / len(shapes)
-    detail = []
-    for j, (name, N, K) in enumerate(shapes):
-        b = linear_bytes(M, N, K) if fused else gemv_bytes(M, N, K)
-        detail.append({"shape": name, "N": N, "K": K, "us": round(per_shape_us[j], 3),
-                       "GB/s": round(b / (per_shape_us[j] * 1e3), 1),
-                       "TOPS": round(2 * M * N * K / (per_shape_us[j] * 1e6), 2)})
-    return dict(ms_step=ms_step, step_bytes=step_bytes, step_ops=step_ops, prod_bytes=prod_bytes,
-                n_prod=n_prod, prod_us_avg=prod_us_avg, detail=detail, resident=resident, setup_s=setup_s,
-                launch="hipGraph" if graph is not None else "eager", fused=fused)
+    return dict(ms_step=ms_step, ms_prod=ms_prod, step_bytes=step_bytes, step_ops=step_ops,
+                prod_bytes=prod_bytes, n_prod=n_prod, resident=resident, setup_s=setup_s,
+                launch="eager" if args.eager else "hipGraph", fused=fused, kernel=kernel)
 
 
 # ----------------------------------------------------------- CPU baseline leg
 def run_cpu_baseline(args, spec):
     """The oracle as it stands, single-threaded, on a bounded sample of the same workload:
-    layer 0's matrices (all four shapes), repeated until about --cpu-seconds of CPU work."""
+    layer 0's matrices (all four shapes; for prefill the first 16 tokens), repeated until
+    about --cpu-seconds of CPU work."""
     import oracle
     from bit_ternary_weight_absmean_amd import synth
 
-    M = spec["M"]
+    M = spec["M"] if not spec["prefill"] else min(spec["M"], 16)
     cfg = spec["cfg"]
     lib = oracle.load()
     mats = []
@@ -236,9 +253,7 @@ def run_cpu_baseline(args, spec):
         g = oracle.absmean(W, lib)
         mats.append((oracle.ternarize(W, g, lib), g, synth.layer_activation(cfg, j, M, K)))
         del W
-    done_bytes = 0
-    done_ops = 0
-    passes = 0
+    done_bytes = done_ops = passes = 0
     t0 = time.perf_counter()
     while True:
         for T, g, X in mats:
@@ -250,15 +265,19 @@ def run_cpu_baseline(args, spec):
             done_ops += 2 * M * N * K
         passes += 1
         el = time.perf_counter() - t0
-        if el >= args.cpu_seconds or (spec["prefill"] and passes >= 1):
+        if el >= args.cpu_seconds:
             break
-    value = done_bytes / el / 1e9 if not spec["prefill"] else done_ops / el / 1e12
-    unit = "GB/s" if not spec["prefill"] else "TOPS"
+    if spec["prefill"]:
+        value, unit = done_ops / el / 1e12, "TOPS"
+    else:
+        value, unit = done_bytes / el / 1e9, "GB/s"
     return {"value": round(value, 4), "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": f"layer 0 of the workload ({len(mats)} matrices, M={M}), {passes} pass(es), "
-                      f"{el:.1f} s single-threaded C oracle (quantize + int32 triple loop + epilogue)"}
+            "sample": f"layer 0 of the workload ({len(mats)} matrices, M={M}), {passes} pass(es) in {el:.1f} s "
+                      "of the single-threaded C oracle (quantize + int32 triple loop + epilogue), bytes and ops "
+                      "counted as for the GPU step"}
 
 
+# ----------------------------------------------------------- counters
 def calib_copy():
     import torch
 
@@ -271,6 +290,77 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes_each_way": 4 * n, "copies": 10}))
 
 
+def _pmc_rows(d, counter):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if r.get("Counter_Name") == counter]
+    return rows
+
+
+def summarize_pmc(args):
+    fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, out_json = args.summarize_pmc
+    spec = workload_spec(args.workload, args.m)
+    if args.split:
+        kernel = "k_gemm" if spec["prefill"] else "k_gemv_direct"
+    else:
+        kernel = "k_gemm" if spec["prefill"] else "k_linear_decode"
+
+    def per_launch_kib(d, counter, match):
+        vals = [float(r["Counter_Value"]) for r in _pmc_rows(d, counter) if match(r["Kernel_Name"])]
+        if not vals:
+            raise SystemExit(f"no {counter} rows for the kernel in {d}")
+        return sum(vals) / len(vals), len(vals)
+
+    def is_kernel(name):
+        return kernel in name
+
+    def is_copy(name):
+        return ("copy" in name.lower() or "elementwise" in name.lower()) and "bt::" not in name
+
+    fetch_kib, n_f = per_launch_kib(fetch_dir, "FETCH_SIZE", is_kernel)
+    write_kib, n_w = per_launch_kib(write_dir, "WRITE_SIZE", is_kernel)
+    cal_fetch_kib, _ = per_launch_kib(cal_fetch_dir, "FETCH_SIZE", is_copy)
+    cal_write_kib, _ = per_launch_kib(cal_write_dir, "WRITE_SIZE", is_copy)
+    copy_bytes = 4 * (1 << 28)
+    f_fetch = copy_bytes / (cal_fetch_kib * 1024)
+    f_write = copy_bytes / (cal_write_kib * 1024)
+    M = spec["M"]
+    alg = [linear_bytes(M, N, K) if kernel == "k_linear_decode" else gemv_bytes(M, N, K)
+           for _, N, K in spec["shapes"]]
+    out = {
+        "kernel": kernel, "workload": spec["desc"], "M": M,
+        "source_sha256": source_hash(kernel),
+        "launches_counted": {"FETCH_SIZE": n_f, "WRITE_SIZE": n_w},
+        "fetch_kib_per_launch_raw": round(fetch_kib, 1), "write_kib_per_launch_raw": round(write_kib, 1),
+        "copy_calibration": {"bytes_each_way": copy_bytes, "FETCH_SIZE_kib": round(cal_fetch_kib, 1),
+                             "WRITE_SIZE_kib": round(cal_write_kib, 1), "fetch_factor": round(f_fetch, 4),
+                             "write_factor": round(f_write, 4)},
+        "traffic_bytes_per_launch": round(fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write),
+        "algorithmic_bytes_per_launch": round(sum(alg) / len(alg)),
+        "command": args.command,
+    }
+    with open(out_json, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
+def traffic_for(spec, kernel):
+    path = traffic_path(spec["name"], kernel, spec["M"])
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != source_hash(kernel):
+        return None  # the kernel changed since the counters were taken
+    return rec["traffic_bytes_per_launch"]
+
+
+# ----------------------------------------------------------------- entry
 def main():
     args = parse()
     if args.gpus != 1:
@@ -278,27 +368,32 @@ def main():
               "(the hot path is a single-GPU kernel; multi-GPU sharding is a design note only).",
               file=sys.stderr)
         return 2
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return 0
     if args.calib_copy:
         calib_copy()
         return 0
     spec = workload_spec(args.workload, args.m)
     g = run_gpu(args, spec)
     M = spec["M"]
+    prod_us = g["ms_prod"] * 1e3 / g["n_prod"]
+    bytes_per_launch = g["prod_bytes"] / g["n_prod"]
+    ops_per_launch = g["step_ops"] / g["n_prod"]
+    traffic = traffic_for(spec, g["kernel"])
     if spec["prefill"]:
         value = g["step_ops"] / (g["ms_step"] * 1e-3) / 1e12
         unit = "TOPS"
-        ach = g["step_ops"] / spec["layers"] / len(spec["shapes"]) / (g["prod_us_avg"] * 1e-6) / 1e12
+        ach = ops_per_launch / (prod_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": None}
+                "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": traffic}
     else:
         value = g["step_bytes"] / (g["ms_step"] * 1e-3) / 1e9
         unit = "GB/s"
-        ach = g["prod_bytes"] / g["n_prod"] / (g["prod_us_avg"] * 1e-6) / 1e9
+        ach = bytes_per_launch / (prod_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = run_cpu_baseline(args, spec)
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, spec)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -317,15 +412,17 @@ def main():
                    "resident_packed_bytes": g["resident"], "launch": g["launch"],
                    "step": ("per matrix: bt_ternary_linear (quantizer fused into the decode kernel)" if g["fused"]
                             else "per matrix: bt_quant_act + " +
-                            ("bt_ternary_gemm" if spec["prefill"] else "bt_ternary_gemv"))},
+                            ("bt_ternary_gemm" if g["kernel"] == "k_gemm" else "bt_ternary_gemv"))},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "detail": {"hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4) if not spec["prefill"] else None,
+        "detail": {"dominant_kernel": g["kernel"], "kernel_avg_us": round(prod_us, 3),
+                   "algorithmic_bytes_per_launch": round(bytes_per_launch),
+                   "ops_per_launch": round(ops_per_launch),
+                   "step_hbm_frac": None if spec["prefill"] else round(value / HBM_PEAK_GBS, 4),
+                   "step_TOPS": round(g["step_ops"] / (g["ms_step"] * 1e-3) / 1e12, 3),
                    "weights_per_s": round(sum(N * K for _, N, K in spec["shapes"]) * spec["layers"] /
                                           (g["ms_step"] * 1e-3), 1),
-                   "step_TOPS": round(g["step_ops"] / (g["ms_step"] * 1e-3) / 1e12, 3),
-                   "product_kernel_avg_us": round(g["prod_us_avg"], 3),
-                   "per_shape": g["detail"], "setup_s": round(g["setup_s"], 1)},
+                   "setup_s": round(g["setup_s"], 1)},
     }
     print(json.dumps(line), flush=True)
     return 0
