@@ -78,7 +78,7 @@ size_t bt_packed_weight_bytes(int64_t N, int64_t K)
     return (size_t)(bt::round_up(N, 64) * bt::round_up(K, 64) / 4);
 }
 
-int64_t bt_act_row_bytes(int64_t K) { return K <= 0 ? 0 : bt::round_up(K, 64); }
+int64_t bt_act_row_bytes(int64_t K) { return K <= 0 ? 0 : bt::round_up(K, 256); }
 
 size_t bt_pack_workspace_bytes(int64_t N, int64_t K)
 {

@@ -8,7 +8,7 @@
 // Per row m: a = max_k |x| (exact, order-free), inv = 127.0f / a (IEEE fp32
 // division, correctly rounded), q = clamp(rint(x * inv), -127, 127) (round half to
 // even), s_x = a / 127.0f and sum_k q. The int8 row is written with stride ldq
-// (K rounded up to 64) and zero padding, four codes per 32-bit store.
+// (K rounded up to 256) and zero padding, four codes per 32-bit store.
 #include "bt_internal.h"
 
 namespace bt {

@@ -25,7 +25,8 @@
  *    (but the kernels still stay in bounds).
  *  - Calls on different streams may run concurrently; a call reads only its
  *    inputs and writes only its outputs. The library holds no mutable global state
- *    other than a thread-local error string.
+ *    other than a thread-local error string and a once-per-process kernel attribute
+ *    (the prefill kernel's LDS cap).
  */
 #ifndef BT_H
 #define BT_H
@@ -68,8 +69,9 @@ typedef int32_t bt_status;
  */
 size_t bt_packed_weight_bytes(int64_t N, int64_t K);
 
-/* Row stride, in bytes, of the int8 activation matrix Xq: K rounded up to 64.
- * Bytes k >= K of each row are zero (bt_quant_act writes them). */
+/* Row stride, in bytes, of the int8 activation matrix Xq: K rounded up to 256 (one
+ * k-step of the product kernels). Bytes k >= K of each row are zero (bt_quant_act
+ * writes them), so the kernels never guard the k tail of an activation row. */
 int64_t bt_act_row_bytes(int64_t K);
 
 /* Workspace, in bytes, that bt_pack_weights needs (fp64 per-row |W| sums). */

@@ -46,8 +46,9 @@ def test_sizes():
     assert L.bt_packed_weight_bytes(100, 300) == 128 * 320 // 4  # padded to 64 x 64
     assert L.bt_packed_weight_bytes(0, 300) == 0
     assert L.bt_act_row_bytes(2560) == 2560
-    assert L.bt_act_row_bytes(300) == 320
-    assert L.bt_act_row_bytes(1) == 64
+    assert L.bt_act_row_bytes(300) == 512
+    assert L.bt_act_row_bytes(1) == 256
+    assert L.bt_act_row_bytes(6912) == 6912
     assert L.bt_act_row_bytes(0) == 0
     assert L.bt_pack_workspace_bytes(3, 5) == 256
     assert L.bt_pack_workspace_bytes(100, 5) == 1024
