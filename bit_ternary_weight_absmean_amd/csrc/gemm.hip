@@ -6,70 +6,176 @@
 // Tiling (gfx950, wave64, v_mfma_i32_16x16x64_i8, 160 KB LDS per CU):
 //  * a workgroup of WM x WN waves computes a BM (tokens) x BN (weight rows) block; each
 //    wave owns a 64 x 64 tile of 4 x 4 MFMA tiles, so every activation operand read
-//    from LDS feeds 4 MFMAs and every unpacked weight operand feeds 4, with the 64
-//    accumulator registers and both operand pipelines within 256 VGPRs (two waves per
-//    SIMD, so one wave's MFMAs cover the other's loads and unpacking).
-//  * k advances 256 per step: lane group g = lane / 16 covers the 64-k chunk 4*step + g,
-//    lane row r = lane % 16.
-//  * weights (B operand): each lane loads its 16 packed bytes per 16-row tile straight
-//    from memory (a 256-byte segment per 16 lanes), one step ahead, and unpacks word j
-//    with shifts and one mask into the operand dwords (word >> 2s) & 0x03030303, whose
-//    byte e is the code of k = 64c + 16j + 4s + e. No LDS is used for weights.
-//  * activations (A operand): the BM x 256 int8 tile is staged in LDS (row pitch 272
-//    bytes: 16-byte reads of 16 rows hit distinct banks), double-buffered, filled from
-//    registers loaded one step ahead; for substep j a lane reads x[m][64c + 16j .. +15],
-//    exactly the A operand that pairs with weight word j. One barrier per step.
-//  * output: lane holds D[4g + v][r] of each tile = token 16a + 4g + v, row 16i + r;
-//    y = (acc - sum_k q) * (gamma * s_x) is stored directly.
+//    from LDS feeds 4 MFMAs and every unpacked weight operand feeds 4.
+//  * k advances BK (128 or 256) per step, in J = BK / 64 MFMA substeps. At substep j,
+//    lane (g, r) with g = lane / 16, r = lane % 16 holds row r's 16 bytes of the 16-k
+//    piece c = g * J + j of the step (k = step * BK + 16 c .. + 15) of both operands:
+//    the activations as int8, the weights as the codes of packed word c % 4 of chunk
+//    step * J + c / 4, unpacked with shifts and one mask into (word >> 2s) & 0x03030303
+//    (byte e of dword s is the code of k = 16 (c % 4) + 4 s + e within the chunk).
+//  * both operand tiles of a step travel HBM/L2 -> LDS by direct loads
+//    (global_load_lds_dwordx4: each lane's 16 bytes land at LDS offset 16 * lane of a
+//    1 KB block), through a ring of NS stages, with no register staging and no LDS
+//    store instructions. A step's loads are issued NS - 1 steps ahead; one barrier per
+//    step both publishes the stage that is about to be read and retires the one that is
+//    about to be refilled.
+//  * LDS layouts read conflict-free (each 16 lanes read 256 contiguous bytes):
+//      activations: [16-row tile][16-k piece of the step][row][16 bytes];
+//      weights:     the packed layout itself, [64-row block][64-k chunk][row][16 bytes].
+//  * output: lane holds D[4g + v][r] of each tile = token 16a + 4g + v, weight row
+//    16i + r; the wave transposes its tile through LDS 16 tokens at a time and stores
+//    y = (acc - sum_k q) * (gamma * s_x) row-contiguously, 16 bytes per lane.
 //  * workgroup -> tile map is XCD-aware: consecutive workgroup ids land on different
-//    XCDs, so the tile order is remapped to give each XCD a contiguous run of tiles that
-//    share activation rows (kept in that XCD's L2).
-#include <atomic>
+//    XCDs, so each XCD is given a contiguous run of a grouped tile order (8 token-tile
+//    rows walked weight-tile column by column): the workgroups resident on an XCD then
+//    share 8 activation panels and 8 weight panels in its L2, instead of streaming a
+//    different weight panel each from HBM.
+#include <type_traits>
 
 #include "bt_internal.h"
 
 namespace bt {
 namespace {
 
-constexpr int kStepK = 256;
-constexpr int kPitch = kStepK + 16;  // LDS row pitch in bytes
 constexpr int kXcds = 8;
+// Token-tile rows per group of the tile order: with two 4-wave workgroups per CU, an
+// XCD's 32 CUs hold 64 workgroups, an 8 x 8 block of tiles.
+#ifndef BT_GEMM_GROUP
+#define BT_GEMM_GROUP 8
+#endif
+constexpr int kGroup = BT_GEMM_GROUP;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_void;
 
 __device__ inline v4i unpack_word(uint32_t w)
 {
     return v4i{(int)(w & kMask0), (int)((w >> 2) & kMask0), (int)((w >> 4) & kMask0), (int)((w >> 6) & kMask0)};
 }
 
-template <int BM, int BN, int WM, int WN>
+// s_waitcnt immediate that waits until at most `vm` vector-memory operations of this
+// wave are outstanding (expcnt and lgkmcnt left at their maxima: no wait on them).
+constexpr int vmcnt_imm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int BM, int BN, int WM, int WN, int NS, int BK>
+struct GemmCfg {
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+    static constexpr int J = BK / 64;                 // MFMA substeps (and 64-k chunks) per step
+    static constexpr int kABytes = BM * BK;           // activation tile per stage
+    static constexpr int kBBytes = BN * BK / 4;       // packed weight tile per stage
+    static constexpr int kStage = kABytes + kBBytes;
+    static constexpr int kLds = NS * kStage;
+    static constexpr int kABlocks = kABytes / 1024;   // 1 KB direct-load blocks
+    static constexpr int kBBlocks = kBBytes / 1024;
+    static constexpr int kAPerWave = kABlocks / kWaves;  // activation blocks per wave per step
+    static constexpr int kBPerWave = kBBlocks / kWaves;  // weight blocks per wave per step
+    static constexpr int kBlocksPerWave = kAPerWave + kBPerWave;
+    static_assert(BM / WM == 64 && BN / WN == 64, "wave tile is 64 x 64");
+    static_assert(BK == 128 || BK == 256, "k step");
+    static_assert(kABlocks % kWaves == 0 && kBBlocks % kWaves == 0, "direct-load blocks split evenly over waves");
+    static_assert(NS >= 2, "at least double buffering");
+};
+
+template <int BM, int BN, int WM, int WN, int NS, int BK>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
-    const float *__restrict__ sx, const int32_t *__restrict__ xsum, int64_t M, int64_t N, int KC, int NB16,
-    int tiles_m, int tiles_n, float *__restrict__ Y, int32_t *__restrict__ ACC)
+    const float *__restrict__ sx, const int32_t *__restrict__ xsum, int64_t M, int64_t N, int KC, int NBLK,
+    int tiles_m, int tiles_n, int group, float *__restrict__ Y, int32_t *__restrict__ ACC, int vec)
 {
-    constexpr int kThreads = WM * WN * 64;
-    constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
-    constexpr int TM = WTM / 16, TN = WTN / 16;
-    constexpr int XL = BM * kStepK / 16 / kThreads;  // 16-byte activation units per thread per step
-    extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [2][BM][kPitch]
+    using C = GemmCfg<BM, BN, WM, WN, NS, BK>;
+    constexpr int TM = C::TM, TN = C::TN, J = C::J;
+    static_assert((C::kWaves / 2) * 16 * 68 * 4 <= C::kStage, "epilogue slabs fit in two stages");
+    static_assert(NS <= 4, "ring of at most four stages");
+    // One LDS array per ring stage ([A tile | B tile] each): distinct objects let the
+    // compiler see that a direct load into one stage cannot alias reads of another, so
+    // it adds no wait of its own between them (the stage index is a compile-time
+    // constant in every unrolled step below).
+    __shared__ __attribute__((aligned(1024))) int8_t lds0[C::kStage];
+    __shared__ __attribute__((aligned(1024))) int8_t lds1[C::kStage];
+    __shared__ __attribute__((aligned(1024))) int8_t lds2[NS > 2 ? C::kStage : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t lds3[NS > 3 ? C::kStage : 16];
+    auto stage_mem = [&](auto sc) -> int8_t * {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (S == 0)
+            return lds0;
+        else if constexpr (S == 1)
+            return lds1;
+        else if constexpr (S == 2)
+            return lds2;
+        else
+            return lds3;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
     const int g = lane >> 4, r = lane & 15;
-    const int nsteps = (KC + 3) >> 2;
+    const int nsteps = (KC + J - 1) / J;
+    const int last = nsteps - 1;
 
-    // XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a contiguous
-    // range of the m-major tile list.
+    // Tile order. Workgroup b runs on XCD b % 8, and each XCD takes a contiguous run of
+    // a grouped tile list: groups of `group` token-tile rows, walked weight-tile column by
+    // column, so the workgroups resident on one XCD at a time cover a compact block of
+    // tiles whose activation and weight panels are shared in that XCD's L2.
     const int total = tiles_m * tiles_n;
     const int per_xcd = (total + kXcds - 1) / kXcds;
     const int b = blockIdx.x;
     const int t = (b % kXcds) * per_xcd + b / kXcds;
     if (t >= total)
         return;
-    const int tm = t / tiles_n, tn = t - tm * tiles_n;
+    const int gsz = group * tiles_n;
+    const int gid = t / gsz, gin = t - gid * gsz;
+    const int gm0 = gid * group;
+    const int grows = min(group, tiles_m - gm0);
+    const int tm = gm0 + gin % grows, tn = gin / grows;
     const int64_t m0 = (int64_t)tm * BM;
-    const int n16_0 = (tn * BN + wn * WTN) / 16;  // first 16-row weight block of this wave
+    const int rb0 = tn * (BN / 64);  // first 64-row weight block of the workgroup
+
+    // This wave's direct-load blocks per step: kAPerWave activation blocks (16-row
+    // tile at, 16-k pieces 4cq .. 4cq + 3: lane L brings row L % 16's piece
+    // 4cq + L / 16), then kBPerWave weight blocks (64-row block rbl, chunk gq of the
+    // step: lane L brings row L's 16 bytes). Each load is a wave-uniform 64-bit base
+    // (advanced per step in scalar registers) plus a loop-invariant per-lane offset.
+    // Rows past M read row M - 1 and blocks past N read the last block: their outputs
+    // are never stored. Chunks past K read the last chunk against zero activations
+    // (activation rows are zero-padded to a multiple of 256 bytes).
+    constexpr int NA = C::kAPerWave, NB = C::kBPerWave;
+    const int8_t *xbase = Xq + m0 * ldq;  // + st * BK per step
+    uint32_t aoff[NA];
+    int adst[NA];
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+        const int blk = wave * NA + q;
+        const int at = blk / J, cq = blk % J;
+        const int64_t m = min(m0 + at * 16 + r, M - 1);
+        aoff[q] = (uint32_t)((m - m0) * ldq + (4 * cq + g) * 16);
+        adst[q] = (at * 4 * J + 4 * cq) * 256;
+    }
+    const int8_t *wrow[NB];  // uniform: start of the weight block's row of chunks
+    int bdst[NB], bchunk[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+        const int blk = wave * NB + q;
+        const int rbl = blk / J, gq = blk % J;
+        wrow[q] = reinterpret_cast<const int8_t *>(Wp) + (int64_t)min(rb0 + rbl, NBLK - 1) * KC * 1024;
+        bdst[q] = C::kABytes + (rbl * J + gq) * 1024;
+        bchunk[q] = gq;
+    }
+    const uint32_t boff = (uint32_t)(lane * 16);
+    auto issue = [&](int st, int8_t *sdst) {
+        const int8_t *xs = xbase + (int64_t)st * BK;
+#pragma unroll
+        for (int q = 0; q < NA; ++q)
+            __builtin_amdgcn_global_load_lds((global_void *)(xs + aoff[q]), (lds_void *)(sdst + adst[q]), 16, 0, 0);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int8_t *ws = wrow[q] + (int64_t)min(J * st + bchunk[q], KC - 1) * 1024;
+            __builtin_amdgcn_global_load_lds((global_void *)(ws + boff), (lds_void *)(sdst + bdst[q]), 16, 0, 0);
+        }
+    };
 
     v4i acc[TM][TN];
 #pragma unroll
@@ -78,151 +184,162 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
         for (int i = 0; i < TN; ++i)
             acc[a][i] = v4i{0, 0, 0, 0};
 
-    // Native vectors, not uint4: copies of HIP's struct vector type through an array
-    // lower to memcpy, which keeps the array in scratch memory.
-    v4i xreg[XL];
-    // Branch-free loads (a divergent guard makes the compiler wait at every join):
-    // rows past M read row M-1 (their outputs are never stored) and activation rows
-    // are zero-padded to a multiple of 256 bytes, so every step's chunks exist.
-    auto load_x = [&](int st) {
-#pragma unroll
-        for (int q = 0; q < XL; ++q) {
-            const int u = tid + q * kThreads;  // 16-byte unit of the BM x 256 tile
-            const int row = u >> 4, col = u & 15;
-            const int64_t m = min(m0 + row, M - 1);
-            xreg[q] = *reinterpret_cast<const v4i *>(Xq + m * ldq + (int64_t)st * kStepK + col * 16);
-        }
-    };
-    auto store_x = [&](int buf) {
-        int8_t *base = xs + buf * BM * kPitch;
-#pragma unroll
-        for (int q = 0; q < XL; ++q) {
-            const int u = tid + q * kThreads;
-            *reinterpret_cast<v4i *>(base + (u >> 4) * kPitch + (u & 15) * 16) = xreg[q];
-        }
-    };
-    // Clamped, unconditional weight loads: a chunk past K meets zero activations (the
-    // activation rows are zero-padded to the step) and a row past N is never stored,
-    // so neither needs the padding code.
-    auto load_w = [&](int st, v4i (&w)[TN]) {
-        const int cc = min(4 * st + g, KC - 1);
+    // LDS read offsets of this lane's operands within a stage: the activation piece
+    // g * J + j of row r of tile a, and row (16 i + r) of the weight chunk g * J / 4.
+    const int a_off = ((wm * TM) * 4 * J + g * J) * 256 + r * 16;                 // + (a * 4J + j) * 256
+    const int b_off = C::kABytes + (wn * J + (g * J) / 4) * 1024 + r * 16;       // + i * 256
+    const int wsel = (g * J) & 3;  // first packed word of the lane's pieces (0, or 0 / 2)
+
+    // One step on ring stage S (a compile-time constant): wait for this step's loads,
+    // refill stage (S + NS - 1) % NS with step st + NS - 1, multiply out stage S.
+    auto step = [&](auto sc, int st) {
+        constexpr int S = decltype(sc)::value;
+        // This wave's loads for step st are done once at most (NS - 2) steps of loads
+        // remain outstanding (vector-memory operations complete in issue order); the
+        // barrier then makes every wave's loads visible and guarantees that the stage
+        // refilled below is no longer being read (every wave consumed its reads of it
+        // in the previous step). A bare s_barrier: __syncthreads() adds a fence that
+        // would wait for all outstanding loads, including the steps still ahead.
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * C::kBlocksPerWave));
+        __builtin_amdgcn_s_barrier();
+        issue(min(st + NS - 1, last), stage_mem(std::integral_constant<int, (S + NS - 1) % NS>{}));
+
+        const int8_t *sp = stage_mem(sc);
+        uint32_t wv[TN][J];
 #pragma unroll
         for (int i = 0; i < TN; ++i) {
-            const int bc = min(n16_0 + i, NB16 - 1);
-            w[i] = reinterpret_cast<const v4i *>(Wp)[((int64_t)(bc >> 2) * KC + cc) * 64 + 16 * (bc & 3) + r];
+            const v4i w4 = *reinterpret_cast<const v4i *>(sp + b_off + i * 256);
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                wv[i][j] = (J == 4) ? (uint32_t)w4[j] : (uint32_t)(wsel ? w4[2 + j] : w4[j]);
         }
-    };
-
-    // One step of MFMAs on LDS buffer `buf` with the weight registers w. The A operands
-    // of substep j + 1 are read while the MFMAs of substep j run.
-    auto compute = [&](int buf, const v4i (&w)[TN]) {
-        const int8_t *xb = xs + buf * BM * kPitch + (wm * WTM + r) * kPitch + g * 64;
-        v4i aop[2][TM];
 #pragma unroll
-        for (int a = 0; a < TM; ++a)
-            aop[0][a] = *reinterpret_cast<const v4i *>(xb + a * 16 * kPitch);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j < 3) {
-#pragma unroll
-                for (int a = 0; a < TM; ++a)
-                    aop[(j + 1) & 1][a] = *reinterpret_cast<const v4i *>(xb + a * 16 * kPitch + (j + 1) * 16);
-            }
-            v4i bop[TN];
-#pragma unroll
-            for (int i = 0; i < TN; ++i) {
-                bop[i] = unpack_word((uint32_t)w[i][j]);
-            }
+        for (int j = 0; j < J; ++j) {
+            v4i aop[TM];
 #pragma unroll
             for (int a = 0; a < TM; ++a)
+                aop[a] = *reinterpret_cast<const v4i *>(sp + a_off + (a * 4 * J + j) * 256);
 #pragma unroll
-                for (int i = 0; i < TN; ++i)
-                    acc[a][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[j & 1][a], bop[i], acc[a][i], 0, 0, 0);
+            for (int i = 0; i < TN; ++i) {
+                const v4i bop = unpack_word(wv[i][j]);
+#pragma unroll
+                for (int a = 0; a < TM; ++a)
+                    acc[a][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[a], bop, acc[a][i], 0, 0, 0);
+            }
         }
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
 
-    // Ping-pong: even steps use weight registers wA and LDS buffer 0, odd steps wB and
-    // buffer 1; the activation registers always hold the step after the one being
-    // computed. Buffer b is rewritten only after the barrier that ends the step that
-    // last read it. The loop body is branch-free (prefetches past the last step reload
-    // the last step, harmlessly), so the compiler's wait counts stay exact and a step
-    // only waits for loads issued a full step earlier.
-    v4i wA[TN], wB[TN];
+    // K = 0 (nsteps = 0): no loads at all (the operand pointers may be null); the
+    // accumulators stay zero.
     if (nsteps > 0) {
-        load_x(0);
-        load_w(0, wA);
-        store_x(0);
-        const int s1 = min(1, nsteps - 1);
-        load_x(s1);
-        load_w(s1, wB);
+        issue(0, lds0);
+        if constexpr (NS > 2)
+            issue(min(1, last), lds1);
+        if constexpr (NS > 3)
+            issue(min(2, last), lds2);
     }
+    // Steps in groups of NS (step st uses stage st % NS), then the remainder.
+    int st = 0;
+    for (; st + NS <= nsteps; st += NS) {
+        step(I0{}, st);
+        step(I1{}, st + 1);
+        if constexpr (NS > 2)
+            step(I2{}, st + 2);
+        if constexpr (NS > 3)
+            step(I3{}, st + 3);
+    }
+    if (st < nsteps)
+        step(I0{}, st);
+    if (st + 1 < nsteps)
+        step(I1{}, st + 1);
+    if constexpr (NS > 3) {
+        if (st + 2 < nsteps)
+            step(I2{}, st + 2);
+    }
+    // Retire the trailing (clamped, unused) loads, then wait until every wave is done
+    // with the stages: the epilogue reuses their LDS.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    const int last = nsteps - 1;
-    const int npairs = nsteps >> 1;
-    for (int p = 0; p < npairs; ++p) {
-        const int st = 2 * p;
-        compute(0, wA);
-        store_x(1);  // the activation registers hold step st + 1
-        load_x(min(st + 2, last));
-        load_w(min(st + 2, last), wA);
-        __syncthreads();
-        compute(1, wB);
-        store_x(0);  // step st + 2 (unused past the last step)
-        load_x(min(st + 3, last));
-        load_w(min(st + 3, last), wB);
-        __syncthreads();
-    }
-    if (nsteps & 1)
-        compute(0, wA);
 
+    // Epilogue: each wave passes its 64 x 64 accumulator tile through a private LDS
+    // slab, 16 tokens at a time, so that stores are row-contiguous (16 bytes per lane
+    // when vec, else 4), instead of the MFMA layout's 4-byte column fragments.
+    // Slab pitch 68 words: the MFMA-layout writes (16 columns x 4 rows per instruction)
+    // and the row reads both hit 64 distinct banks.
+    constexpr int kPitchW = 68;
+    // (the first half of the waves in stage 0's memory, the second half in stage 1's)
+    constexpr int kHalf = C::kWaves / 2;
+    int32_t *slab = reinterpret_cast<int32_t *>(wave < kHalf ? lds0 : lds1) + (wave % kHalf) * 16 * kPitchW;
     const float gamma = w_scale[0];
+    const int64_t n0 = (int64_t)tn * BN + wn * 64;
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t m = m0 + wm * WTM + a * 16 + 4 * g + v;
-            if (m >= M)
-                continue;
-            const int32_t xs_m = xsum[m];
-            const float scale = gamma * sx[m];
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-            for (int i = 0; i < TN; ++i) {
-                const int64_t n = (int64_t)(n16_0 + i) * 16 + r;
-                if (n >= N)
-                    continue;
-                const int accv = acc[a][i][v] - xs_m;
-                if (ACC)
-                    ACC[m * N + n] = accv;
-                if (Y)
-                    Y[m * N + n] = (float)accv * scale;
+            for (int i = 0; i < TN; ++i)
+                slab[(4 * g + v) * kPitchW + 16 * i + r] = acc[a][i][v];
+        const int64_t mt = m0 + wm * 64 + a * 16;  // first token of this 16-row slab
+        if (vec) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rr = 4 * q + g;  // slab row of this lane
+                const int64_t m = mt + rr;
+                const int64_t n = n0 + 4 * r;
+                const v4i a4 = *reinterpret_cast<const v4i *>(slab + rr * kPitchW + 4 * r);
+                if (m < M && n < N) {
+                    const int32_t xs_m = xsum[m];
+                    const float scale = gamma * sx[m];
+                    const v4i d = a4 - xs_m;
+                    if (ACC)
+                        *reinterpret_cast<v4i *>(ACC + m * N + n) = d;
+                    if (Y) {
+                        float4 y;
+                        y.x = (float)d[0] * scale;
+                        y.y = (float)d[1] * scale;
+                        y.z = (float)d[2] * scale;
+                        y.w = (float)d[3] * scale;
+                        *reinterpret_cast<float4 *>(Y + m * N + n) = y;
+                    }
+                }
+            }
+        } else {
+            for (int rr = 0; rr < 16; ++rr) {
+                const int64_t m = mt + rr;
+                const int64_t n = n0 + lane;
+                const int32_t a1 = slab[rr * kPitchW + lane];
+                if (m < M && n < N) {
+                    const int32_t d = a1 - xsum[m];
+                    if (ACC)
+                        ACC[m * N + n] = d;
+                    if (Y)
+                        Y[m * N + n] = (float)d * (gamma * sx[m]);
+                }
             }
         }
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NS, int BK>
 hipError_t launch_t(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
                     const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
 {
+    using C = GemmCfg<BM, BN, WM, WN, NS, BK>;
     const int KC = (int)((K + 63) / 64);
-    const int NB16 = (int)(((N + 63) / 64) * 4);
+    const int NBLK = (int)((N + 63) / 64);
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     const int total = tiles_m * tiles_n;
     const int per_xcd = (total + kXcds - 1) / kXcds;
-    const size_t lds = (size_t)2 * BM * kPitch;
-    // Raising this kernel's dynamic-LDS cap is idempotent; do it once per process.
-    static std::atomic<bool> attr_set{false};
-    if (lds > 64 * 1024 && !attr_set.load(std::memory_order_acquire)) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<BM, BN, WM, WN>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess)
-            return e;
-        attr_set.store(true, std::memory_order_release);
-    }
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN>), dim3((unsigned)(per_xcd * kXcds)), dim3(WM * WN * 64), lds, s, Wp,
-                       w_scale, Xq,
-                       ldq, sx, xsum, M, N, KC, NB16, tiles_m, tiles_n, Y, acc);
+    // 16-byte output stores need every row start 16-byte aligned.
+    const int vec = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) &&
+                    (reinterpret_cast<uintptr_t>(acc) % 16 == 0);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, BK>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0, s, Wp, w_scale, Xq, ldq, sx, xsum, M, N, KC, NBLK, tiles_m, tiles_n, kGroup, Y,
+                       acc, vec);
     return hipGetLastError();
 }
 
@@ -231,13 +348,16 @@ hipError_t launch_t(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int
 hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
                        const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
 {
-    // 128 x 256 blocks (8 waves) share each staged activation tile between twice as
-    // many weight rows; they win once there are enough of them to occupy most CUs.
-    // With fewer tiles the 128 x 128 blocks (4 waves) spread the work wider.
+    // Measured on the 2B-class prefill shapes (M = 256 and 2048):
+    //  * 128 x 256 blocks (8 waves, one workgroup per CU, 3-stage ring of 256-k steps)
+    //    share each staged activation tile between the most weight rows; best when the
+    //    tiles make about one round over the 256 CUs;
+    //  * otherwise 64 x 256 blocks (4 waves, two workgroups per CU, 4-stage ring of
+    //    128-k steps), which keep more tiles in flight and hide load latency deeper.
     const int64_t t128x256 = ((M + 127) / 128) * ((N + 255) / 256);
-    if (t128x256 >= 192)
-        return launch_t<128, 256, 2, 4>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
-    return launch_t<128, 128, 2, 2>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    if (t128x256 >= 128 && t128x256 <= 256)
+        return launch_t<128, 256, 2, 4, 3, 256>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    return launch_t<64, 256, 1, 4, 4, 128>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
 }
 
 }  // namespace bt
