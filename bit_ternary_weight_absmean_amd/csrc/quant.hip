@@ -1,4 +1,7 @@
 // Fused per-token absmax int8 activation quantizer: one workgroup per token row.
+// Rows of up to 32768 floats (16-byte aligned, K % 4 == 0) stay in registers between
+// the absmax and the quantize pass (the row is read from memory once); other rows
+// take a two-pass kernel that re-reads the row from cache.
 //
 // BitNet GPU guide ("How to Run BitNet Inference on GPU Using CUDA Kernels"),
 // "Understanding the Two-Phase Architecture": activations are quantized to INT8
@@ -110,13 +113,98 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(const float *__restrict_
     }
 }
 
+// Register-resident variant: thread t holds float4 chunks t, t + 256, ... (at most C).
+// Loads are clamped and masked rather than guarded, so they all issue before the
+// first wait.
+template <int C>
+__global__ __launch_bounds__(kThreads) void k_quant_act_reg(const float *__restrict__ X, int64_t K, int64_t ldq,
+                                                            int8_t *__restrict__ Xq, float *__restrict__ sx,
+                                                            int32_t *__restrict__ xsum)
+{
+    __shared__ float red_f[kThreads / 64];
+    __shared__ int red_i[kThreads / 64];
+    const int tid = threadIdx.x;
+    const int64_t m = blockIdx.x;
+    const float4 *x = reinterpret_cast<const float4 *>(X + m * K);
+    const int nch = (int)(K >> 2);  // float4 chunks in the row (>= 1)
+
+    float4 v[C];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int idx = tid + c * kThreads;
+        const float4 t = x[min(idx, nch - 1)];
+        const bool in = idx < nch;
+        v[c].x = in ? t.x : 0.0f;
+        v[c].y = in ? t.y : 0.0f;
+        v[c].z = in ? t.z : 0.0f;
+        v[c].w = in ? t.w : 0.0f;
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[c].x), fabsf(v[c].y)), fmaxf(fabsf(v[c].z), fabsf(v[c].w))));
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0)
+        red_f[tid >> 6] = amax;
+    __syncthreads();
+    amax = red_f[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w)
+        amax = fmaxf(amax, red_f[w]);
+
+    const bool zero = (amax == 0.0f);
+    const float inv = zero ? 0.0f : 127.0f / amax;
+    uint32_t *q = reinterpret_cast<uint32_t *>(Xq + m * ldq);
+    int sum = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int idx = tid + c * kThreads;
+        const int e0 = quant_one(v[c].x, inv), e1 = quant_one(v[c].y, inv);
+        const int e2 = quant_one(v[c].z, inv), e3 = quant_one(v[c].w, inv);
+        sum += e0 + e1 + e2 + e3;
+        if (idx < nch)
+            q[idx] = (uint32_t)(e0 & 0xff) | ((uint32_t)(e1 & 0xff) << 8) | ((uint32_t)(e2 & 0xff) << 16) |
+                     ((uint32_t)(e3 & 0xff) << 24);
+    }
+    // Zero padding up to ldq (a multiple of 4 bytes, as K is here).
+    for (int64_t idx = nch + tid; idx < (ldq >> 2); idx += kThreads)
+        q[idx] = 0u;
+    sum = wave_sum(sum);
+    if ((tid & 63) == 0)
+        red_i[tid >> 6] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int total = 0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w)
+            total += red_i[w];
+        sx[m] = zero ? 0.0f : amax / 127.0f;
+        xsum[m] = total;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int64_t ldq, int8_t *Xq, float *sx,
                             int32_t *xsum, hipStream_t s)
 {
-    if (M > 0)
-        hipLaunchKernelGGL(k_quant_act, dim3((unsigned)M), dim3(kThreads), 0, s, X, K, ldq, Xq, sx, xsum);
+    if (M <= 0)
+        return hipGetLastError();
+    const dim3 grid((unsigned)M), block(kThreads);
+    const bool reg = K > 0 && (K % 4) == 0 && (reinterpret_cast<uintptr_t>(X) % 16) == 0;
+    const int64_t per_thread = (K / 4 + kThreads - 1) / kThreads;  // float4 chunks per thread
+    if (reg && per_thread <= 1)
+        hipLaunchKernelGGL(k_quant_act_reg<1>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+    else if (reg && per_thread <= 2)
+        hipLaunchKernelGGL(k_quant_act_reg<2>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+    else if (reg && per_thread <= 4)
+        hipLaunchKernelGGL(k_quant_act_reg<4>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+    else if (reg && per_thread <= 8)
+        hipLaunchKernelGGL(k_quant_act_reg<8>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+    else if (reg && per_thread <= 16)
+        hipLaunchKernelGGL(k_quant_act_reg<16>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+    else if (reg && per_thread <= 32)
+        hipLaunchKernelGGL(k_quant_act_reg<32>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+    else
+        hipLaunchKernelGGL(k_quant_act, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
     return hipGetLastError();
 }
 

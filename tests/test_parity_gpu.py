@@ -99,7 +99,8 @@ def test_pack_zero_matrix():
 
 
 # ------------------------------------------------------------------ quant
-QUANT_SHAPES = [(1, 1), (1, 7), (3, 300), (128, 256), (1, 2560), (1, 28672), (5, 6912), (2048, 2560)]
+QUANT_SHAPES = [(1, 1), (1, 7), (3, 300), (1, 4), (2, 1028), (128, 256), (1, 2560), (1, 28672), (5, 6912),
+                (2048, 2560), (3, 32768), (2, 40000)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES)
