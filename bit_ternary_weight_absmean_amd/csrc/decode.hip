@@ -72,11 +72,23 @@ __device__ inline void mfma_step(const uint4 (&w)[RB], const int32_t (&xw)[16], 
     }
 }
 
-// Weight uint4 of block b16, chunk c, lane row r (padding words outside the matrix).
-__device__ inline uint4 load_w(const uint4 *__restrict__ Wp, int b16, int NB16, int c, int KC, int r, bool ok)
+// Weight uint4 of block b16, chunk c, lane row r, from a clamped, always valid address
+// (callers load only with KC >= 1). Slots outside the matrix get padding words where
+// the value is used (mask_w), not here: a select or a branch right after a load makes
+// the compiler wait for that load before it issues the next one.
+__device__ inline v4i load_w_raw(const uint4 *__restrict__ Wp, int b16, int NB16, int c, int KC, int r)
 {
-    return (ok && b16 < NB16) ? Wp[((int64_t)(b16 >> 2) * KC + c) * 64 + 16 * (b16 & 3) + r]
-                              : make_uint4(kPadWord, kPadWord, kPadWord, kPadWord);
+    const int bb = min(b16, NB16 - 1), cc = min(max(c, 0), KC - 1);
+    return reinterpret_cast<const v4i *>(Wp)[((int64_t)(bb >> 2) * KC + cc) * 64 + 16 * (bb & 3) + r];
+}
+
+// The loaded words where keep, else four padding words (sixteen zero weights).
+__device__ inline uint4 mask_w(const v4i &w, bool keep)
+{
+    const int k = keep ? -1 : 0;
+    const int pad = (int)kPadWord & ~k;
+    return make_uint4((uint32_t)((w[0] & k) | pad), (uint32_t)((w[1] & k) | pad), (uint32_t)((w[2] & k) | pad),
+                      (uint32_t)((w[3] & k) | pad));
 }
 
 __device__ inline void unpack16(const uint4 (&v)[4], int32_t (&xw)[16])
@@ -145,28 +157,39 @@ __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct(
         a1[k] = a4[k] = a16[k] = v4i{0, 0, 0, 0};
 
     for (int i0 = 0; i0 < nmine; i0 += U) {
-        uint4 w[U][RB];
-        uint4 xv[U][4];
+        // Every load of the batch first, at clamped addresses; the masks where used.
+        v4i w[U][RB];
+        v4i xv[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int i = i0 + u;
-            const int c = 4 * (wave + WAVES * i) + g;
-            const bool ok = (i < nmine) && (c < KC);
+            const int c = 4 * (wave + WAVES * (i0 + u)) + g;
 #pragma unroll
             for (int k = 0; k < RB; ++k)
-                w[u][k] = load_w(Wp, blockIdx.x * RB + k, NB16, c, KC, r, ok);
-            const uint4 *p = reinterpret_cast<const uint4 *>(Xq + (int64_t)r * ldq + (int64_t)c * 64);
+                w[u][k] = load_w_raw(Wp, blockIdx.x * RB + k, NB16, c, KC, r);
+            const v4i *p = reinterpret_cast<const v4i *>(Xq + (int64_t)min(r, M - 1) * ldq +
+                                                         (int64_t)min(c, KC - 1) * 64);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                xv[u][q] = (ok && r < M) ? p[q] : make_uint4(0, 0, 0, 0);
+                xv[u][q] = p[q];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (i0 + u >= nmine)
                 break;
+            const int c = 4 * (wave + WAVES * (i0 + u)) + g;
+            const int keep = (c < KC && r < M) ? -1 : 0;
+            uint4 xk[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xk[q] = make_uint4((uint32_t)(xv[u][q][0] & keep), (uint32_t)(xv[u][q][1] & keep),
+                                   (uint32_t)(xv[u][q][2] & keep), (uint32_t)(xv[u][q][3] & keep));
             int32_t xw[16];
-            unpack16(xv[u], xw);
-            mfma_step<RB>(w[u], xw, a1, a4, a16);
+            unpack16(xk, xw);
+            uint4 wm[RB];
+#pragma unroll
+            for (int k = 0; k < RB; ++k)
+                wm[k] = mask_w(w[u][k], c < KC && blockIdx.x * RB + k < NB16);
+            mfma_step<RB>(wm, xw, a1, a4, a16);
         }
     }
 #pragma unroll
@@ -188,8 +211,11 @@ __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct(
 // and the k-split w % S of it: steps st = w % S, w % S + S, ... For S = 1 a wave owns
 // all of K and its epilogue runs straight from its MFMA registers; for S > 1 the S
 // partial sums of a block are added through LDS. MT = compile-time token capacity
-// (M <= MT); RPT float4 of each token per thread stay in registers for the quantizer.
-template <int MT, int S, bool VEC>
+// (M <= MT). RX > 0: each thread keeps RX float4 of each token in registers for the
+// quantizer (the launcher picks the smallest power of two that covers K, so the loads
+// need no guards); RX = 0: the tokens are streamed from memory twice (large or
+// unaligned K).
+template <int MT, int S, int RX>
 __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const float *__restrict__ X, int M, int64_t N,
     int K, int KC, int NB16, float *__restrict__ Y, int32_t *__restrict__ ACC)
@@ -197,7 +223,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     constexpr int WAVES = kFusedWaves;
     constexpr int T = WAVES * 64;
     constexpr int U = 4;              // steps per register batch
-    constexpr int RPT = kXRegs / MT;
+    constexpr int RPT = RX > 0 ? RX : 1;
     constexpr int RBW = WAVES / S;    // row blocks per workgroup
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float *s_apart = reinterpret_cast<float *>(smem);                  // [WAVES][kMaxM]
@@ -218,52 +244,62 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     const int nb = (nmine + U - 1) / U;
 
     const int K4 = (K + 3) >> 2;
-    const int R = (K4 + T - 1) / T;
-    const bool regpath = VEC && R <= RPT;
+    constexpr bool regpath = RX > 0;  // then K4 >= 1 and K4 <= RX * T (the launcher checks)
 
     auto load4 = [&](const float *xr, int k4) -> float4 {
-        if (VEC)
+        if (K % 4 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0)
             return reinterpret_cast<const float4 *>(xr)[k4];
         const int k = 4 * k4;
         return make_float4(xr[k], (k + 1 < K) ? xr[k + 1] : 0.0f, (k + 2 < K) ? xr[k + 2] : 0.0f,
                            (k + 3 < K) ? xr[k + 3] : 0.0f);
     };
 
-    // 1. Activations first (waiting for them then does not wait for the weights). Each
-    //    slot is one load at a clamped, always valid address and a select.
+    // 1. Activations first (waiting for them then does not wait for the weights): RX
+    //    unconditional loads per token at clamped addresses (tokens past M re-read
+    //    token M - 1); the masks are applied in step 3, where the values are used.
+    v4i xraw[MT][RPT];
+    if constexpr (regpath) {
+        const v4i *X4 = reinterpret_cast<const v4i *>(X);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < RPT; ++i)
+                xraw[m][i] = X4[(int64_t)min(m, M - 1) * K4 + min(tid + i * T, K4 - 1)];
+        // Keep them ahead of the weight loads in issue order: the quantizer then waits
+        // for the activations only (vector-memory operations complete in order).
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 2. The wave's first weight batch.
+    v4i wa[U], wb[U];
+    auto load_batch = [&](v4i (&w)[U], int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            w[u] = load_w_raw(Wp, b16, NB16, 4 * (ks + S * (b * U + u)) + g, KC, r);
+    };
+    if constexpr (regpath) {
+        // K >= 4, so KC >= 1 and the clamped addresses are valid: no guard (a branch
+        // here would make the quantizer's wait cover the weight loads as well).
+        load_batch(wa, 0);
+        load_batch(wb, 1);
+    } else {
+        if (nb > 0)
+            load_batch(wa, 0);
+        if (nb > 1)
+            load_batch(wb, 1);
+    }
+
+    // 3. Per-token absmax: wave partials in LDS.
     float4 xr[MT][RPT];
-    if (regpath) {
-        const float4 *X4 = reinterpret_cast<const float4 *>(X);
+    if constexpr (regpath) {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                xr[m][i] = make_float4(0, 0, 0, 0);
-                if (m < M && i < R) {  // uniform
-                    const int k4 = tid + i * T;
-                    const float4 v = X4[(int64_t)m * K4 + min(k4, K4 - 1)];
-                    xr[m][i] = (k4 < K4) ? v : make_float4(0, 0, 0, 0);
-                }
+                const int keep = (m < M && tid + i * T < K4) ? -1 : 0;
+                xr[m][i] = make_float4(__int_as_float(xraw[m][i][0] & keep), __int_as_float(xraw[m][i][1] & keep),
+                                       __int_as_float(xraw[m][i][2] & keep), __int_as_float(xraw[m][i][3] & keep));
             }
-    }
-
-    // 2. The wave's first weight batch.
-    uint4 wa[U], wb[U];
-    auto load_batch = [&](uint4 (&w)[U], int b) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = b * U + u;
-            const int c = 4 * (ks + S * i) + g;
-            w[u] = load_w(Wp, b16, NB16, c, KC, r, (i < nmine) && (c < KC));
-        }
-    };
-    if (nb > 0)
-        load_batch(wa, 0);
-    if (nb > 1)
-        load_batch(wb, 1);
-
-    // 3. Per-token absmax: wave partials in LDS.
-    if (regpath) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if (m < M) {  // a guard, not a break: the loop must stay fully unrolled
@@ -301,7 +337,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
             amax = fmaxf(amax, s_apart[w * kMaxM + m]);
         return amax;
     };
-    if (regpath) {
+    if constexpr (regpath) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if (m < M) {
@@ -348,7 +384,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     // 5. Stream the wave's weights, two batches in flight, MFMAs on the older one.
     v4i a1[1], a4[1], a16[1];
     a1[0] = a4[0] = a16[0] = v4i{0, 0, 0, 0};
-    auto compute_batch = [&](const uint4 (&w)[U], int b) {
+    auto compute_batch = [&](const v4i (&w)[U], int b) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = b * U + u;
@@ -364,7 +400,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
                 }
                 int32_t xw[16];
                 unpack16(xv, xw);
-                const uint4 wk[1] = {w[u]};
+                const uint4 wk[1] = {mask_w(w[u], c < KC && b16 < NB16)};
                 mfma_step<1>(wk, xw, a1, a4, a16);
             }
         }
@@ -454,24 +490,41 @@ size_t fused_lds(int64_t M, int64_t K, int s)
     return 2 * kFusedWaves * kMaxM * 4 + (s > 1 ? kFusedWaves * 256 * 4 : 0) + (size_t)M * (KC * 64 + kPitchPad);
 }
 
-template <int MT, int S>
-hipError_t launch_fused_t(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
-                          float *Y, int32_t *acc, hipStream_t s)
+template <int MT, int S, int RX>
+hipError_t launch_fused_rx(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+                           float *Y, int32_t *acc, hipStream_t s)
 {
     constexpr int RBW = kFusedWaves / S;
     const int KC = (int)((K + 63) / 64);
     const int NB16 = (int)(((N + 63) / 64) * 4);
     const int64_t nb16 = (N + 15) / 16;
     const dim3 grid((unsigned)((nb16 + RBW - 1) / RBW)), block(kFusedWaves * 64);
-    const size_t lds = fused_lds(M, K, S);
-    const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-    if (vec)
-        hipLaunchKernelGGL((k_linear_decode<MT, S, true>), grid, block, lds, s, Wp, w_scale, X, (int)M, N, (int)K,
-                           KC, NB16, Y, acc);
-    else
-        hipLaunchKernelGGL((k_linear_decode<MT, S, false>), grid, block, lds, s, Wp, w_scale, X, (int)M, N,
-                           (int)K, KC, NB16, Y, acc);
+    hipLaunchKernelGGL((k_linear_decode<MT, S, RX>), grid, block, fused_lds(M, K, S), s, Wp, w_scale, X, (int)M, N,
+                       (int)K, KC, NB16, Y, acc);
     return hipGetLastError();
+}
+
+// Register path when the rows are 16-byte aligned with K % 4 == 0 and each thread's
+// share fits kXRegs float4 over all MT tokens: RX = the smallest power of two with
+// RX * 512 >= K / 4.
+template <int MT, int S>
+hipError_t launch_fused_t(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+                          float *Y, int32_t *acc, hipStream_t s)
+{
+    const int64_t K4 = K / 4, T = kFusedWaves * 64;
+    const bool vec = K > 0 && (K & 3) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
+    int rx = 1;
+    while ((int64_t)rx * T < K4)
+        rx *= 2;
+    if (!vec || rx * MT > kXRegs)
+        return launch_fused_rx<MT, S, 0>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    switch (rx) {
+    case 1: return launch_fused_rx<MT, S, 1>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    case 2: return launch_fused_rx<MT, S, (MT <= 8 ? 2 : 1)>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    case 4: return launch_fused_rx<MT, S, (MT <= 4 ? 4 : 1)>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    case 8: return launch_fused_rx<MT, S, (MT <= 2 ? 8 : 1)>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    default: return launch_fused_rx<MT, S, (MT <= 1 ? 16 : 1)>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    }
 }
 
 template <int MT>
