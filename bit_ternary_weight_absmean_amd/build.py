@@ -35,6 +35,9 @@ COMMON_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     # Keep the compiler from emitting packed fp32 VALU ops.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Kernel arguments arrive preloaded in SGPRs (gfx950): a decode launch does not wait
+    # on a kernarg memory load before it can form its first addresses.
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wno-unused-command-line-argument",
     "-I", INCLUDE,
     "-I", CSRC,
