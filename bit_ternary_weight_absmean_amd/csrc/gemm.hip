@@ -24,7 +24,8 @@
 //      weights:     the packed layout itself, [64-row block][64-k chunk][row][16 bytes].
 //  * output: lane holds D[4g + v][r] of each tile = token 16a + 4g + v, weight row
 //    16i + r; the wave transposes its tile through LDS 16 tokens at a time and stores
-//    y = (acc - sum_k q) * (gamma * s_x) row-contiguously, 16 bytes per lane.
+//    y = (acc - sum_k q) * (gamma * s_x) row-contiguously, 16 bytes per lane, with
+//    non-temporal stores.
 //  * workgroup -> tile map is XCD-aware: consecutive workgroup ids land on different
 //    XCDs, so each XCD is given a contiguous run of a grouped tile order (8 token-tile
 //    rows walked weight-tile column by column): the workgroups resident on an XCD then
@@ -46,6 +47,7 @@ constexpr int kXcds = 8;
 constexpr int kGroup = BT_GEMM_GROUP;
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const void global_void;
 
 __device__ inline v4i unpack_word(uint32_t w)
@@ -276,6 +278,15 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
     int32_t *slab = reinterpret_cast<int32_t *>(wave < kHalf ? lds0 : lds1) + (wave % kHalf) * 16 * kPitchW;
     const float gamma = w_scale[0];
     const int64_t n0 = (int64_t)tn * BN + wn * 64;
+    // Row statistics of the lane's 16 rows in one batch (clamped rows): one round trip.
+    int32_t xs_r[TM * 4];
+    float sx_r[TM * 4];
+#pragma unroll
+    for (int c = 0; c < TM * 4; ++c) {
+        const int64_t m = min(m0 + wm * 64 + (c >> 2) * 16 + 4 * (c & 3) + g, M - 1);
+        xs_r[c] = xsum[m];
+        sx_r[c] = sx[m];
+    }
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
 #pragma unroll
@@ -292,18 +303,17 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
                 const int64_t n = n0 + 4 * r;
                 const v4i a4 = *reinterpret_cast<const v4i *>(slab + rr * kPitchW + 4 * r);
                 if (m < M && n < N) {
-                    const int32_t xs_m = xsum[m];
-                    const float scale = gamma * sx[m];
+                    const int32_t xs_m = xs_r[4 * a + q];
+                    const float scale = gamma * sx_r[4 * a + q];
                     const v4i d = a4 - xs_m;
+                    // Non-temporal: the output is not read again by this kernel, and
+                    // streaming it past the caches measured 3-9% faster here.
                     if (ACC)
-                        *reinterpret_cast<v4i *>(ACC + m * N + n) = d;
+                        __builtin_nontemporal_store(d, reinterpret_cast<v4i *>(ACC + m * N + n));
                     if (Y) {
-                        float4 y;
-                        y.x = (float)d[0] * scale;
-                        y.y = (float)d[1] * scale;
-                        y.z = (float)d[2] * scale;
-                        y.w = (float)d[3] * scale;
-                        *reinterpret_cast<float4 *>(Y + m * N + n) = y;
+                        const v4f y = {(float)d[0] * scale, (float)d[1] * scale, (float)d[2] * scale,
+                                       (float)d[3] * scale};
+                        __builtin_nontemporal_store(y, reinterpret_cast<v4f *>(Y + m * N + n));
                     }
                 }
             }
@@ -315,9 +325,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
                 if (m < M && n < N) {
                     const int32_t d = a1 - xsum[m];
                     if (ACC)
-                        ACC[m * N + n] = d;
+                        __builtin_nontemporal_store(d, ACC + m * N + n);
                     if (Y)
-                        Y[m * N + n] = (float)d * (gamma * sx[m]);
+                        __builtin_nontemporal_store((float)d * (gamma * sx[m]), Y + m * N + n);
                 }
             }
         }

@@ -158,7 +158,10 @@ def test_gemv_small(M, N, K, algo):
     check_product(gpu_pack(W), gpu_quant(X), ref, M, N, bt.ternary_gemv, algo=algo)
 
 
-GEMM_SMALL = [(1, 64, 64), (17, 100, 300), (128, 512, 256), (129, 130, 129), (300, 200, 517), (64, 1000, 2560)]
+# (257, 516, 700): ragged 64 x 256 tiles in both dimensions with both outputs;
+# (1024, 8448, 512): 528 tiles, more than one round of workgroups.
+GEMM_SMALL = [(1, 64, 64), (17, 100, 300), (128, 512, 256), (129, 130, 129), (300, 200, 517), (64, 1000, 2560),
+              (257, 516, 700), (1024, 8448, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SMALL)
