@@ -232,6 +232,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     int8_t *xq = reinterpret_cast<int8_t *>(red + (S > 1 ? WAVES * 256 : 0));
     const int pitch = KC * 64 + kPitchPad;
 
+    const float gamma = w_scale[0];  // issued first: the epilogue needs it last
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
@@ -337,12 +338,16 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
             amax = fmaxf(amax, s_apart[w * kMaxM + m]);
         return amax;
     };
+    // absmax of the token this lane's output column holds (token r), for the epilogue.
+    float amax_r = 0.0f;
     if constexpr (regpath) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if (m < M) {
                 const float amax = token_amax(m);
                 const float inv = (amax == 0.0f) ? 0.0f : 127.0f / amax;
+                if (m == r)
+                    amax_r = amax;
                 int8_t *qrow = xq + m * pitch;
                 int sum = 0;
 #pragma unroll
@@ -366,6 +371,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
         for (int m = 0; m < M; ++m) {
             const float amax = token_amax(m);
             const float inv = (amax == 0.0f) ? 0.0f : 127.0f / amax;
+            if (m == r)
+                amax_r = amax;
             int8_t *qrow = xq + m * pitch;
             const float *xm = X + (int64_t)m * K;
             int sum = 0;
@@ -439,14 +446,11 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
         }
     }
     if (ks == 0 && r < M) {
-        float amax = s_apart[r];
         int qs = s_qpart[r];
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w) {
-            amax = fmaxf(amax, s_apart[w * kMaxM + r]);
+        for (int w = 1; w < WAVES; ++w)
             qs += s_qpart[w * kMaxM + r];
-        }
-        const float scale = w_scale[0] * ((amax == 0.0f) ? 0.0f : amax / 127.0f);
+        const float scale = gamma * ((amax_r == 0.0f) ? 0.0f : amax_r / 127.0f);
         const int64_t n0 = (int64_t)b16 * 16 + 4 * g;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
