@@ -215,14 +215,15 @@ __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct(
 // quantizer (the launcher picks the smallest power of two that covers K, so the loads
 // need no guards); RX = 0: the tokens are streamed from memory twice (large or
 // unaligned K).
-template <int MT, int S, int RX>
+template <int MT, int S, int RX, int U>
 __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const float *__restrict__ X, int M, int64_t N,
     int K, int KC, int NB16, float *__restrict__ Y, int32_t *__restrict__ ACC)
 {
     constexpr int WAVES = kFusedWaves;
     constexpr int T = WAVES * 64;
-    constexpr int U = 4;              // steps per register batch
+    // U: steps per register batch (two batches in flight), sized by the launcher to the
+    // steps a wave owns, so the first two batches hold few clamped duplicate loads.
     constexpr int RPT = RX > 0 ? RX : 1;
     constexpr int RBW = WAVES / S;    // row blocks per workgroup
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -494,18 +495,32 @@ size_t fused_lds(int64_t M, int64_t K, int s)
     return 2 * kFusedWaves * kMaxM * 4 + (s > 1 ? kFusedWaves * 256 * 4 : 0) + (size_t)M * (KC * 64 + kPitchPad);
 }
 
-template <int MT, int S, int RX>
-hipError_t launch_fused_rx(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
-                           float *Y, int32_t *acc, hipStream_t s)
+template <int MT, int S, int RX, int U>
+hipError_t launch_fused_u(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+                          float *Y, int32_t *acc, hipStream_t s)
 {
     constexpr int RBW = kFusedWaves / S;
     const int KC = (int)((K + 63) / 64);
     const int NB16 = (int)(((N + 63) / 64) * 4);
     const int64_t nb16 = (N + 15) / 16;
     const dim3 grid((unsigned)((nb16 + RBW - 1) / RBW)), block(kFusedWaves * 64);
-    hipLaunchKernelGGL((k_linear_decode<MT, S, RX>), grid, block, fused_lds(M, K, S), s, Wp, w_scale, X, (int)M, N,
-                       (int)K, KC, NB16, Y, acc);
+    hipLaunchKernelGGL((k_linear_decode<MT, S, RX, U>), grid, block, fused_lds(M, K, S), s, Wp, w_scale, X, (int)M,
+                       N, (int)K, KC, NB16, Y, acc);
     return hipGetLastError();
+}
+
+// Batch size: the steps of 256 k a wave owns (at most ceil(steps / S)) over two batches.
+template <int MT, int S, int RX>
+hipError_t launch_fused_rx(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+                           float *Y, int32_t *acc, hipStream_t s)
+{
+    const int64_t steps = (K + 255) / 256;
+    const int64_t mine = (steps + S - 1) / S;
+    if (mine <= 2)
+        return launch_fused_u<MT, S, RX, 1>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    if (mine <= 4)
+        return launch_fused_u<MT, S, RX, 2>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    return launch_fused_u<MT, S, RX, 4>(Wp, w_scale, X, M, N, K, Y, acc, s);
 }
 
 // Register path when the rows are 16-byte aligned with K % 4 == 0 and each thread's
