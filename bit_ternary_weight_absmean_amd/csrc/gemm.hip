@@ -7,21 +7,26 @@
 //  * a workgroup of WM x WN waves computes a BM (tokens) x BN (weight rows) block; each
 //    wave owns a 64 x 64 tile of 4 x 4 MFMA tiles, so every activation operand read
 //    from LDS feeds 4 MFMAs and every unpacked weight operand feeds 4.
-//  * k advances BK (128 or 256) per step, in J = BK / 64 MFMA substeps. At substep j,
-//    lane (g, r) with g = lane / 16, r = lane % 16 holds row r's 16 bytes of the 16-k
-//    piece c = g * J + j of the step (k = step * BK + 16 c .. + 15) of both operands:
-//    the activations as int8, the weights as the codes of packed word c % 4 of chunk
-//    step * J + c / 4, unpacked with shifts and one mask into (word >> 2s) & 0x03030303
-//    (byte e of dword s is the code of k = 16 (c % 4) + 4 s + e within the chunk).
+//  * k advances 128 per step, in two MFMA substeps j = 0, 1 of 64 k. At substep j, lane
+//    (g, r) with g = lane / 16, r = lane % 16 holds row r's 16 bytes of the 16-k piece
+//    p = 2 g + j of the step (k = step * 128 + 16 p .. + 15) of both operands: the
+//    activations as int8, the weights as packed word p % 4 of chunk p / 4 (the lane's
+//    two words of a step are adjacent: one 8-byte LDS read), unpacked with shifts and one
+//    mask into (word >> 2s) & 0x03030303 (byte e of dword s is the code of
+//    k = 16 (p % 4) + 4 s + e within the chunk).
 //  * both operand tiles of a step travel HBM/L2 -> LDS by direct loads
 //    (global_load_lds_dwordx4: each lane's 16 bytes land at LDS offset 16 * lane of a
 //    1 KB block), through a ring of NS stages, with no register staging and no LDS
-//    store instructions. A step's loads are issued NS - 1 steps ahead; one barrier per
-//    step both publishes the stage that is about to be read and retires the one that is
-//    about to be refilled.
-//  * LDS layouts read conflict-free (each 16 lanes read 256 contiguous bytes):
-//      activations: [16-row tile][16-k piece of the step][row][16 bytes];
+//    store instructions. Each lane quad of a load reads one 64-byte segment (adjacent
+//    lanes, adjacent addresses): scattering a quad over rows measured 10% slower.
+//  * LDS layouts, read without bank conflicts:
+//      activations: per 16-row tile, two 1 KB halves of 8 rows x 128 bytes; row rho of
+//                   half h keeps piece p in 16-byte slot p ^ rho ^ h;
 //      weights:     the packed layout itself, [64-row block][64-k chunk][row][16 bytes].
+//  * software pipeline: a lane's substep-1 operands are read while its substep-0 MFMAs
+//    run; one barrier per step, between the two substeps, publishes the next step's
+//    stage and frees the current one for the load NS steps ahead; the next step's
+//    substep-0 operands are then read while this step's substep-1 MFMAs run.
 //  * output: lane holds D[4g + v][r] of each tile = token 16a + 4g + v, weight row
 //    16i + r; the wave transposes its tile through LDS 16 tokens at a time and stores
 //    y = (acc - sum_k q) * (gamma * s_x) row-contiguously, 16 bytes per lane, with
@@ -29,7 +34,7 @@
 //  * workgroup -> tile map is XCD-aware: consecutive workgroup ids land on different
 //    XCDs, so each XCD is given a contiguous run of a grouped tile order (8 token-tile
 //    rows walked weight-tile column by column): the workgroups resident on an XCD then
-//    share 8 activation panels and 8 weight panels in its L2, instead of streaming a
+//    share 8 activation panels and a few weight panels in its L2, instead of streaming a
 //    different weight panel each from HBM.
 #include <type_traits>
 
@@ -59,37 +64,34 @@ __device__ inline v4i unpack_word(uint32_t w)
 // wave are outstanding (expcnt and lgkmcnt left at their maxima: no wait on them).
 constexpr int vmcnt_imm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-template <int BM, int BN, int WM, int WN, int NS, int BK>
+constexpr int kBK = 128;  // k per step
+template <int BM, int BN, int WM, int WN, int NS>
 struct GemmCfg {
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = kWaves * 64;
     static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
-    static constexpr int J = BK / 64;                 // MFMA substeps (and 64-k chunks) per step
-    static constexpr int kABytes = BM * BK;           // activation tile per stage
-    static constexpr int kBBytes = BN * BK / 4;       // packed weight tile per stage
+    static constexpr int kABytes = BM * kBK;          // activation tile per stage
+    static constexpr int kBBytes = BN * kBK / 4;      // packed weight tile per stage
     static constexpr int kStage = kABytes + kBBytes;
-    static constexpr int kLds = NS * kStage;
     static constexpr int kABlocks = kABytes / 1024;   // 1 KB direct-load blocks
     static constexpr int kBBlocks = kBBytes / 1024;
     static constexpr int kAPerWave = kABlocks / kWaves;  // activation blocks per wave per step
     static constexpr int kBPerWave = kBBlocks / kWaves;  // weight blocks per wave per step
     static constexpr int kBlocksPerWave = kAPerWave + kBPerWave;
     static_assert(BM / WM == 64 && BN / WN == 64, "wave tile is 64 x 64");
-    static_assert(BK == 128 || BK == 256, "k step");
     static_assert(kABlocks % kWaves == 0 && kBBlocks % kWaves == 0, "direct-load blocks split evenly over waves");
-    static_assert(NS >= 2, "at least double buffering");
+    static_assert(NS >= 2 && NS <= 4, "ring of two to four stages");
+    static_assert((kWaves / 2) * 16 * 68 * 4 <= kStage, "epilogue slabs fit in two stages");
 };
 
-template <int BM, int BN, int WM, int WN, int NS, int BK>
-__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm(
+template <int BM, int BN, int WM, int WN, int NS, int WPE>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void k_gemm(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
     const float *__restrict__ sx, const int32_t *__restrict__ xsum, int64_t M, int64_t N, int KC, int NBLK,
     int tiles_m, int tiles_n, int group, float *__restrict__ Y, int32_t *__restrict__ ACC, int vec)
 {
-    using C = GemmCfg<BM, BN, WM, WN, NS, BK>;
-    constexpr int TM = C::TM, TN = C::TN, J = C::J;
-    static_assert((C::kWaves / 2) * 16 * 68 * 4 <= C::kStage, "epilogue slabs fit in two stages");
-    static_assert(NS <= 4, "ring of at most four stages");
+    using C = GemmCfg<BM, BN, WM, WN, NS>;
+    constexpr int TM = C::TM, TN = C::TN;
     // One LDS array per ring stage ([A tile | B tile] each): distinct objects let the
     // compiler see that a direct load into one stage cannot alias reads of another, so
     // it adds no wait of its own between them (the stage index is a compile-time
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
     const int wave = uniform(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
     const int g = lane >> 4, r = lane & 15;
-    const int nsteps = (KC + J - 1) / J;
+    const int nsteps = (KC + 1) / 2;  // 128-k steps (two 64-k chunks each)
     const int last = nsteps - 1;
 
     // Tile order. Workgroup b runs on XCD b % 8, and each XCD takes a contiguous run of
@@ -136,45 +138,46 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
     const int64_t m0 = (int64_t)tm * BM;
     const int rb0 = tn * (BN / 64);  // first 64-row weight block of the workgroup
 
-    // This wave's direct-load blocks per step: kAPerWave activation blocks (16-row
-    // tile at, 16-k pieces 4cq .. 4cq + 3: lane L brings row L % 16's piece
-    // 4cq + L / 16), then kBPerWave weight blocks (64-row block rbl, chunk gq of the
-    // step: lane L brings row L's 16 bytes). Each load is a wave-uniform 64-bit base
-    // (advanced per step in scalar registers) plus a loop-invariant per-lane offset.
-    // Rows past M read row M - 1 and blocks past N read the last block: their outputs
-    // are never stored. Chunks past K read the last chunk against zero activations
-    // (activation rows are zero-padded to a multiple of 256 bytes).
+    // This wave's direct-load blocks per step. Activation block (16-row tile at, half h):
+    // lane L brings row 16 at + 8 h + L / 8, the piece that slot L % 8 of that row holds
+    // (slot ^ row ^ h). Weight block (64-row block rbl, chunk gq of the step): lane L
+    // brings row L's 16 bytes. Each load is a wave-uniform 64-bit base (advanced per step
+    // in scalar registers) plus a loop-invariant per-lane offset. Rows past M read row
+    // M - 1 and blocks past N read the last block: their outputs are never stored. Chunks
+    // past K read the last chunk against zero activations (activation rows are
+    // zero-padded to a multiple of 256 bytes).
     constexpr int NA = C::kAPerWave, NB = C::kBPerWave;
-    const int8_t *xbase = Xq + m0 * ldq;  // + st * BK per step
+    const int8_t *xbase = Xq + m0 * ldq;  // + st * 128 per step
     uint32_t aoff[NA];
     int adst[NA];
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
         const int blk = wave * NA + q;
-        const int at = blk / J, cq = blk % J;
-        const int64_t m = min(m0 + at * 16 + r, M - 1);
-        aoff[q] = (uint32_t)((m - m0) * ldq + (4 * cq + g) * 16);
-        adst[q] = (at * 4 * J + 4 * cq) * 256;
+        const int at = blk >> 1, h = blk & 1;
+        const int rho = lane >> 3, slot = lane & 7;
+        const int64_t m = min(m0 + at * 16 + 8 * h + rho, M - 1);
+        aoff[q] = (uint32_t)((m - m0) * ldq + (slot ^ rho ^ h) * 16);
+        adst[q] = blk * 1024;
     }
     const int8_t *wrow[NB];  // uniform: start of the weight block's row of chunks
     int bdst[NB], bchunk[NB];
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
         const int blk = wave * NB + q;
-        const int rbl = blk / J, gq = blk % J;
+        const int rbl = blk >> 1, gq = blk & 1;
         wrow[q] = reinterpret_cast<const int8_t *>(Wp) + (int64_t)min(rb0 + rbl, NBLK - 1) * KC * 1024;
-        bdst[q] = C::kABytes + (rbl * J + gq) * 1024;
+        bdst[q] = C::kABytes + blk * 1024;
         bchunk[q] = gq;
     }
     const uint32_t boff = (uint32_t)(lane * 16);
     auto issue = [&](int st, int8_t *sdst) {
-        const int8_t *xs = xbase + (int64_t)st * BK;
+        const int8_t *xs = xbase + (int64_t)st * kBK;
 #pragma unroll
         for (int q = 0; q < NA; ++q)
             __builtin_amdgcn_global_load_lds((global_void *)(xs + aoff[q]), (lds_void *)(sdst + adst[q]), 16, 0, 0);
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-            const int8_t *ws = wrow[q] + (int64_t)min(J * st + bchunk[q], KC - 1) * 1024;
+            const int8_t *ws = wrow[q] + (int64_t)min(2 * st + bchunk[q], KC - 1) * 1024;
             __builtin_amdgcn_global_load_lds((global_void *)(ws + boff), (lds_void *)(sdst + bdst[q]), 16, 0, 0);
         }
     };
@@ -186,49 +189,71 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
         for (int i = 0; i < TN; ++i)
             acc[a][i] = v4i{0, 0, 0, 0};
 
-    // LDS read offsets of this lane's operands within a stage: the activation piece
-    // g * J + j of row r of tile a, and row (16 i + r) of the weight chunk g * J / 4.
-    const int a_off = ((wm * TM) * 4 * J + g * J) * 256 + r * 16;                 // + (a * 4J + j) * 256
-    const int b_off = C::kABytes + (wn * J + (g * J) / 4) * 1024 + r * 16;       // + i * 256
-    const int wsel = (g * J) & 3;  // first packed word of the lane's pieces (0, or 0 / 2)
-
-    // One step on ring stage S (a compile-time constant): wait for this step's loads,
-    // refill stage (S + NS - 1) % NS with step st + NS - 1, multiply out stage S.
-    auto step = [&](auto sc, int st) {
-        constexpr int S = decltype(sc)::value;
-        // This wave's loads for step st are done once at most (NS - 2) steps of loads
-        // remain outstanding (vector-memory operations complete in issue order); the
-        // barrier then makes every wave's loads visible and guarantees that the stage
-        // refilled below is no longer being read (every wave consumed its reads of it
-        // in the previous step). A bare s_barrier: __syncthreads() adds a fence that
-        // would wait for all outstanding loads, including the steps still ahead.
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * C::kBlocksPerWave));
-        __builtin_amdgcn_s_barrier();
-        issue(min(st + NS - 1, last), stage_mem(std::integral_constant<int, (S + NS - 1) % NS>{}));
-
-        const int8_t *sp = stage_mem(sc);
-        uint32_t wv[TN][J];
+    // LDS read offsets within a stage. Activations: row r of the wave's tile a is row
+    // rho = r % 8 of half r / 8 (+ a * 2048); piece 2 g + j sits in slot (2 g + j) ^ c with
+    // c = rho ^ (r / 8). Weights: words 2 (g & 1), +1 of chunk g / 2 of row 16 i + r
+    // (+ i * 256).
+    const int hr = r >> 3, rho_r = r & 7, c = rho_r ^ hr;
+    const int a_row = ((wm * TM) * 2 + hr) * 1024 + rho_r * 128;
+    const int a_off0 = a_row + ((2 * g) ^ c) * 16;      // substep 0
+    const int a_off1 = a_row + ((2 * g + 1) ^ c) * 16;  // substep 1
+    const int b_off = C::kABytes + (wn * 2 + (g >> 1)) * 1024 + r * 16 + 8 * (g & 1);
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    v4i fa0[TM], fa1[TM];  // activation operands of substeps 0 and 1
+    v2u fb[TN], fbn[TN];   // weight words of this step and of the next
+    auto read_a = [&](const int8_t *sp, int off, v4i (&fa)[TM]) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+            fa[a] = *reinterpret_cast<const v4i *>(sp + off + a * 2048);
+    };
+    auto read_b = [&](const int8_t *sp, v2u (&f)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+            f[i] = *reinterpret_cast<const v2u *>(sp + b_off + i * 256);
+    };
+    auto mma = [&](const v4i (&fa)[TM], const v2u (&f)[TN], int j) {
 #pragma unroll
         for (int i = 0; i < TN; ++i) {
-            const v4i w4 = *reinterpret_cast<const v4i *>(sp + b_off + i * 256);
-#pragma unroll
-            for (int j = 0; j < J; ++j)
-                wv[i][j] = (J == 4) ? (uint32_t)w4[j] : (uint32_t)(wsel ? w4[2 + j] : w4[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            v4i aop[TM];
+            const v4i bop = unpack_word(f[i][j]);
 #pragma unroll
             for (int a = 0; a < TM; ++a)
-                aop[a] = *reinterpret_cast<const v4i *>(sp + a_off + (a * 4 * J + j) * 256);
-#pragma unroll
-            for (int i = 0; i < TN; ++i) {
-                const v4i bop = unpack_word(wv[i][j]);
-#pragma unroll
-                for (int a = 0; a < TM; ++a)
-                    acc[a][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[a], bop, acc[a][i], 0, 0, 0);
-            }
+                acc[a][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[a], bop, acc[a][i], 0, 0, 0);
         }
+    };
+    // The barrier: a bare s_barrier after an explicit wait (__syncthreads() adds a fence
+    // that would wait for every outstanding load, the steps still ahead included), with
+    // compiler-only memory clobbers so that no LDS access moves across it.
+    auto barrier = [] {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // Before step st's barrier this wave's loads of steps st + 1 .. st + NS - 1 are
+    // outstanding; waiting until at most NS - 2 steps of them remain (vector-memory
+    // operations complete in issue order) lands step st + 1, and lgkmcnt(0) retires this
+    // wave's reads of the current stage.
+    constexpr int kWaitStep = vmcnt_imm((NS - 2) * C::kBlocksPerWave) & ~(0xF << 8);
+
+    // One step on ring stage S (a compile-time constant), with substep-0 operands of step
+    // st already in fa0 / fb.
+    auto step = [&](auto sc, int st) {
+        constexpr int S = decltype(sc)::value;
+        int8_t *sp = stage_mem(sc);
+        read_a(sp, a_off1, fa1);
+        mma(fa0, fb, 0);
+        __builtin_amdgcn_s_waitcnt(kWaitStep);
+        barrier();
+        // Every wave is past its reads of stage S: refill it with step st + NS (clamped
+        // to the last step, whose reloaded copy is never read), then read step st + 1's
+        // substep-0 operands from the next stage.
+        issue(min(st + NS, last), sp);
+        int8_t *sn = stage_mem(std::integral_constant<int, (S + 1) % NS>{});
+        read_a(sn, a_off0, fa0);
+        read_b(sn, fbn);
+        mma(fa1, fb, 1);
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+            fb[i] = fbn[i];
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -239,28 +264,33 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
     // accumulators stay zero.
     if (nsteps > 0) {
         issue(0, lds0);
+        issue(min(1, last), lds1);
         if constexpr (NS > 2)
-            issue(min(1, last), lds1);
-        if constexpr (NS > 3)
             issue(min(2, last), lds2);
-    }
-    // Steps in groups of NS (step st uses stage st % NS), then the remainder.
-    int st = 0;
-    for (; st + NS <= nsteps; st += NS) {
-        step(I0{}, st);
-        step(I1{}, st + 1);
-        if constexpr (NS > 2)
-            step(I2{}, st + 2);
         if constexpr (NS > 3)
-            step(I3{}, st + 3);
-    }
-    if (st < nsteps)
-        step(I0{}, st);
-    if (st + 1 < nsteps)
-        step(I1{}, st + 1);
-    if constexpr (NS > 3) {
-        if (st + 2 < nsteps)
-            step(I2{}, st + 2);
+            issue(min(3, last), lds3);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * C::kBlocksPerWave));
+        barrier();
+        read_a(lds0, a_off0, fa0);
+        read_b(lds0, fb);
+        // Steps in groups of NS (step st uses stage st % NS), then the remainder.
+        int st = 0;
+        for (; st + NS <= nsteps; st += NS) {
+            step(I0{}, st);
+            step(I1{}, st + 1);
+            if constexpr (NS > 2)
+                step(I2{}, st + 2);
+            if constexpr (NS > 3)
+                step(I3{}, st + 3);
+        }
+        if (st < nsteps)
+            step(I0{}, st);
+        if (st + 1 < nsteps)
+            step(I1{}, st + 1);
+        if constexpr (NS > 3) {
+            if (st + 2 < nsteps)
+                step(I2{}, st + 2);
+        }
     }
     // Retire the trailing (clamped, unused) loads, then wait until every wave is done
     // with the stages: the epilogue reuses their LDS.
@@ -334,11 +364,11 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int BK>
+template <int BM, int BN, int WM, int WN, int NS, int WPE>
 hipError_t launch_t(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
                     const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
 {
-    using C = GemmCfg<BM, BN, WM, WN, NS, BK>;
+    using C = GemmCfg<BM, BN, WM, WN, NS>;
     const int KC = (int)((K + 63) / 64);
     const int NBLK = (int)((N + 63) / 64);
     const int tiles_m = (int)((M + BM - 1) / BM);
@@ -348,8 +378,8 @@ hipError_t launch_t(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int
     // 16-byte output stores need every row start 16-byte aligned.
     const int vec = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(acc) % 16 == 0);
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, BK>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0, s, Wp, w_scale, Xq, ldq, sx, xsum, M, N, KC, NBLK, tiles_m, tiles_n, kGroup, Y,
-                       acc, vec);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, WPE>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0, s,
+                       Wp, w_scale, Xq, ldq, sx, xsum, M, N, KC, NBLK, tiles_m, tiles_n, kGroup, Y, acc, vec);
     return hipGetLastError();
 }
 
@@ -358,16 +388,11 @@ hipError_t launch_t(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int
 hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
                        const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
 {
-    // Measured on the 2B-class prefill shapes (M = 256 and 2048):
-    //  * 128 x 256 blocks (8 waves, one workgroup per CU, 3-stage ring of 256-k steps)
-    //    share each staged activation tile between the most weight rows; best when the
-    //    tiles make about one round over the 256 CUs;
-    //  * otherwise 64 x 256 blocks (4 waves, two workgroups per CU, 4-stage ring of
-    //    128-k steps), which keep more tiles in flight and hide load latency deeper.
-    const int64_t t128x256 = ((M + 127) / 128) * ((N + 255) / 256);
-    if (t128x256 >= 128 && t128x256 <= 256)
-        return launch_t<128, 256, 2, 4, 3, 256>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
-    return launch_t<64, 256, 1, 4, 4, 128>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    // 64 x 256 blocks of 4 waves, three workgroups per CU (3-stage ring, 48 KB of LDS
+    // each): with three waves per SIMD one wave's LDS reads, unpacking and barrier wait
+    // hide under the others' MFMAs. Measured on the 2B-class prefill shapes against
+    // 128 x 256 blocks of 8 waves and against two workgroups per CU with a 4-stage ring.
+    return launch_t<64, 256, 1, 4, 3, 3>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
 }
 
 }  // namespace bt
