@@ -6,9 +6,10 @@
 A step is one pass of the whole per-call hot path over one batch of synthetic input:
 for every resident weight matrix, quantize its fp32 activations per token to int8, run
 the integer ternary product and apply the scale epilogue -- one bt_ternary_linear call
-per matrix (a single fused kernel at decode sizes; bt_quant_act + bt_ternary_gemm for
-prefill). ``--split`` times the unfused route (bt_quant_act + bt_ternary_gemv/gemm as
-two launches) instead. Weight packing is offline and outside the timed region. Inputs
+per matrix (a single fused kernel at decode sizes; bt_quant_act + bt_ternary_gemm_ws for
+prefill, which splits K over several workgroups per tile where the tiles alone would
+leave the GPU idle). ``--split`` times the same two launches called one by one
+(bt_quant_act + bt_ternary_gemv / bt_ternary_gemm_ws) instead. Weight packing is offline and outside the timed region. Inputs
 are resident in HBM before timing starts; the step is replayed as one HIP graph.
 Prints ONE JSON line.
 
@@ -151,7 +152,7 @@ def run_gpu(args, spec):
     resident = sum(p.data.numel() for row in packed for p in row)
 
     # Per-matrix-type activations, output buffers and (route permitting) workspaces.
-    xs, qs, ys, wss = [], [], [], []
+    xs, qs, ys, wss, gws = [], [], [], [], []
     for j, (_, N, K) in enumerate(shapes):
         X = torch.from_numpy(synth.layer_activation(cfg, j, M, K)).to(dev)
         xs.append(X)
@@ -159,6 +160,8 @@ def run_gpu(args, spec):
         ys.append(torch.empty((M, N), dtype=torch.float32, device=dev))
         wb = bt.linear_workspace_bytes(M, N, K)
         wss.append(torch.empty(wb, dtype=torch.uint8, device=dev) if wb else None)
+        # zero-filled split-K workspace for direct bt_ternary_gemm_ws calls (None: no split)
+        gws.append(bt.gemm_workspace(M, N, K, dev) if M > bt.GEMV_MAX_M else None)
     torch.cuda.synchronize()
 
     fused = (not args.split) and all(bt.linear_workspace_bytes(M, N, K) == 0 for _, N, K in shapes)
@@ -168,14 +171,18 @@ def run_gpu(args, spec):
         kernel = "k_gemm"
     else:
         kernel = "k_gemv_direct"
-    product = bt.ternary_gemm if kernel == "k_gemm" else bt.ternary_gemv
+
+    def product(pw, q, out_y, j):
+        if kernel == "k_gemm":
+            return bt.ternary_gemm(pw, q, out_y=out_y, workspace=gws[j])
+        return bt.ternary_gemv(pw, q, out_y=out_y)
 
     def step():
         for row in packed:
             for j, pw in enumerate(row):
                 if args.split:
                     bt.quant_act(xs[j], out=qs[j])
-                    product(pw, qs[j], out_y=ys[j])
+                    product(pw, qs[j], ys[j], j)
                 else:
                     bt.linear(xs[j], pw, out_y=ys[j], workspace=wss[j])
 
@@ -186,7 +193,7 @@ def run_gpu(args, spec):
                 if fused:
                     bt.linear(xs[j], pw, out_y=ys[j])
                 else:
-                    product(pw, qs[j], out_y=ys[j])
+                    product(pw, qs[j], ys[j], j)
 
     stream = torch.cuda.Stream(device=dev)
 
@@ -411,8 +418,9 @@ def main():
                    "shapes": [f"{n} {N}x{K}" for n, N, K in spec["shapes"]],
                    "resident_packed_bytes": g["resident"], "launch": g["launch"],
                    "step": ("per matrix: bt_ternary_linear (quantizer fused into the decode kernel)" if g["fused"]
-                            else "per matrix: bt_quant_act + " +
-                            ("bt_ternary_gemm" if g["kernel"] == "k_gemm" else "bt_ternary_gemv"))},
+                            else ("per matrix: bt_quant_act + " if args.split else
+                                  "per matrix: bt_ternary_linear = bt_quant_act + ") +
+                            ("bt_ternary_gemm_ws" if g["kernel"] == "k_gemm" else "bt_ternary_gemv"))},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {"dominant_kernel": g["kernel"], "kernel_avg_us": round(prod_us, 3),

@@ -16,6 +16,8 @@ from .api import (
     GEMV_MFMA,
     PackedWeight,
     act_row_bytes,
+    gemm_workspace,
+    gemm_workspace_bytes,
     linear,
     linear_workspace_bytes,
     pack_weights,
@@ -29,6 +31,6 @@ from .api import (
 
 __all__ = [
     "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_MFMA", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
-    "linear", "linear_workspace_bytes", "pack_weights", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
+    "gemm_workspace", "gemm_workspace_bytes", "linear", "linear_workspace_bytes", "pack_weights", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
     "ternary_gemv", "unpack_weights",
 ]

@@ -93,7 +93,7 @@ def quant_act(X: torch.Tensor, out=None):
     return Xq, sx, xsum
 
 
-def _product(fn_name, pw: PackedWeight, q, want_y, want_acc, out_y, out_acc, algo=None):
+def _product(fn_name, pw: PackedWeight, q, want_y, want_acc, out_y, out_acc, algo=None, extra=()):
     Xq, sx, xsum = q
     M = sx.shape[0]
     dev = pw.data.device
@@ -104,6 +104,7 @@ def _product(fn_name, pw: PackedWeight, q, want_y, want_acc, out_y, out_acc, alg
     args = [_ptr(pw.data), _ptr(pw.scale), _ptr(Xq), _ptr(sx), _ptr(xsum), M, pw.N, pw.K, _ptr(Y), _ptr(acc)]
     if algo is not None:
         args.append(algo)
+    args.extend(extra)
     check(getattr(lib(), fn_name)(*args, _stream(dev)))
     return Y, acc
 
@@ -113,9 +114,29 @@ def ternary_gemv(pw: PackedWeight, q, want_y=True, want_acc=False, out_y=None, o
     return _product("bt_ternary_gemv_algo", pw, q, want_y, want_acc, out_y, out_acc, algo)
 
 
-def ternary_gemm(pw: PackedWeight, q, want_y=True, want_acc=False, out_y=None, out_acc=None):
-    """bt_ternary_gemm: prefill product on int8 MFMA for any M. Returns (Y, acc)."""
-    return _product("bt_ternary_gemm", pw, q, want_y, want_acc, out_y, out_acc)
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    """bt_gemm_workspace_bytes: workspace the split-K route of bt_ternary_gemm_ws uses (0: none)."""
+    return int(lib().bt_gemm_workspace_bytes(M, N, K))
+
+
+def gemm_workspace(M: int, N: int, K: int, device) -> torch.Tensor | None:
+    """A zero-filled workspace for bt_ternary_gemm_ws(M, N, K), or None when the shape does not split."""
+    n = gemm_workspace_bytes(M, N, K)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def ternary_gemm(pw: PackedWeight, q, want_y=True, want_acc=False, out_y=None, out_acc=None,
+                 workspace: torch.Tensor | None = None):
+    """bt_ternary_gemm: prefill product on int8 MFMA for any M. Returns (Y, acc).
+
+    With a workspace (see gemm_workspace) the call is bt_ternary_gemm_ws, which splits K
+    over several workgroups per tile where that pays; results are identical.
+    """
+    if workspace is None:
+        return _product("bt_ternary_gemm", pw, q, want_y, want_acc, out_y, out_acc)
+    nbytes = workspace.numel() * workspace.element_size()
+    return _product("bt_ternary_gemm_ws", pw, q, want_y, want_acc, out_y, out_acc,
+                    extra=(_ptr(workspace), nbytes))
 
 
 def linear_workspace_bytes(M: int, N: int, K: int) -> int:

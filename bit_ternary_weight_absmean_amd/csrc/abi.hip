@@ -143,7 +143,7 @@ bt_status bt_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *
         return fail(BT_ERR_ALIGN, "X, x_scale and x_sum must be 4-byte aligned");
     if (Xq && !aligned(Xq, 16))
         return fail(BT_ERR_ALIGN, "Xq must be 16-byte aligned");
-    return hip_status(bt::launch_quant_act(X, M, K, bt_act_row_bytes(K), Xq, x_scale, x_sum,
+    return hip_status(bt::launch_quant_act(X, M, K, bt_act_row_bytes(K), Xq, x_scale, x_sum, nullptr, 0,
                                            static_cast<hipStream_t>(stream)),
                       "bt_quant_act launch");
 }
@@ -180,17 +180,34 @@ bt_status bt_ternary_gemv(const void *Wp, const float *w_scale, const int8_t *Xq
     return bt_ternary_gemv_algo(Wp, w_scale, Xq, x_scale, x_sum, M, N, K, Y, acc, BT_GEMV_AUTO, stream);
 }
 
-bt_status bt_ternary_gemm(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
-                          const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *stream)
+size_t bt_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > BT_MAX_K)
+        return 0;
+    return bt::gemm_workspace_bytes(M, N, K);
+}
+
+bt_status bt_ternary_gemm_ws(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
+                             const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                             void *workspace, size_t workspace_bytes, void *stream)
 {
     if (bt_status s = check_product(Wp, w_scale, Xq, x_scale, x_sum, M, N, K, Y, acc))
         return s;
+    if (workspace && !aligned(workspace, 256))
+        return fail(BT_ERR_ALIGN, "workspace must be 256-byte aligned");
     if (M == 0 || N == 0)
         return ok();
     const int64_t ldq = bt_act_row_bytes(K);
     return hip_status(bt::launch_gemm(static_cast<const uint4 *>(Wp), w_scale, Xq, ldq, x_scale, x_sum, M, N, K, Y,
-                                      acc, static_cast<hipStream_t>(stream)),
+                                      acc, workspace, workspace ? workspace_bytes : 0,
+                                      static_cast<hipStream_t>(stream)),
                       "bt_ternary_gemm launch");
+}
+
+bt_status bt_ternary_gemm(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
+                          const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *stream)
+{
+    return bt_ternary_gemm_ws(Wp, w_scale, Xq, x_scale, x_sum, M, N, K, Y, acc, nullptr, 0, stream);
 }
 
 // Largest LDS footprint the fused decode kernel is launched with.
@@ -201,11 +218,19 @@ static bool linear_fused(int64_t M, int64_t N, int64_t K)
     return M <= BT_GEMV_MAX_M && bt::decode_fused_lds_bytes(M, N, K) <= kFusedLdsLimit;
 }
 
+// Workspace of the unfused route: [Xq | x_scale | x_sum | split-K GEMM workspace], each
+// part 256-byte aligned.
+static size_t linear_quant_bytes(int64_t M, int64_t K)
+{
+    return (size_t)(bt::round_up(M * bt_act_row_bytes(K), 256) + 2 * bt::round_up(4 * M, 256));
+}
+
 size_t bt_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || N <= 0 || K < 0 || linear_fused(M, N, K))
         return 0;
-    return (size_t)(bt::round_up(M * bt_act_row_bytes(K), 256) + 2 * bt::round_up(4 * M, 256));
+    const size_t gemm = M > BT_GEMV_MAX_M ? bt_gemm_workspace_bytes(M, N, K) : 0;
+    return linear_quant_bytes(M, K) + gemm;
 }
 
 bt_status bt_ternary_linear(const void *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
@@ -236,11 +261,21 @@ bt_status bt_ternary_linear(const void *Wp, const float *w_scale, const float *X
     int8_t *Xq = static_cast<int8_t *>(workspace);
     float *sx = reinterpret_cast<float *>(Xq + bt::round_up(M * bt_act_row_bytes(K), 256));
     int32_t *xsum = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(sx) + bt::round_up(4 * M, 256));
-    if (bt_status st = bt_quant_act(X, M, K, Xq, sx, xsum, stream))
-        return st;
-    if (M <= BT_GEMV_MAX_M)
+    if (M <= BT_GEMV_MAX_M) {
+        if (bt_status st = bt_quant_act(X, M, K, Xq, sx, xsum, stream))
+            return st;
         return bt_ternary_gemv_algo(Wp, w_scale, Xq, sx, xsum, M, N, K, Y, acc, BT_GEMV_MFMA, stream);
-    return bt_ternary_gemm(Wp, w_scale, Xq, sx, xsum, M, N, K, Y, acc, stream);
+    }
+    // The quantizer also zero-fills the split-K arrival counters of the GEMM workspace,
+    // so the caller's workspace needs no initialization.
+    char *gws = static_cast<char *>(workspace) + linear_quant_bytes(M, K);
+    const size_t gbytes = bt_gemm_workspace_bytes(M, N, K);
+    if (bt_status st = hip_status(bt::launch_quant_act(X, M, K, bt_act_row_bytes(K), Xq, sx, xsum,
+                                                       reinterpret_cast<unsigned *>(gws),
+                                                       gbytes ? bt::gemm_arrival_words(M, N) : 0, s),
+                                  "bt_quant_act launch"))
+        return st;
+    return bt_ternary_gemm_ws(Wp, w_scale, Xq, sx, xsum, M, N, K, Y, acc, gbytes ? gws : nullptr, gbytes, stream);
 }
 
 const char *bt_status_str(bt_status s)

@@ -41,8 +41,10 @@ __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v);
 hipError_t launch_pack(const float *W, int64_t N, int64_t K, uint4 *Wp, float *gamma, double *rowsum,
                        hipStream_t s);
 hipError_t launch_unpack(const uint4 *Wp, int64_t N, int64_t K, int8_t *T, hipStream_t s);
+// The quantizer also zero-fills `clear_words` 32-bit words at `clear` (split-K arrival
+// counters of the product that follows it; NULL / 0 for none).
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int64_t ldq, int8_t *Xq, float *sx,
-                            int32_t *xsum, hipStream_t s);
+                            int32_t *xsum, unsigned *clear, int64_t clear_words, hipStream_t s);
 hipError_t launch_gemv_dot4(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq,
                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
                             int32_t *acc, hipStream_t s);
@@ -53,8 +55,15 @@ hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, const int8_t 
 hipError_t launch_linear_decode(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N,
                                 int64_t K, float *Y, int32_t *acc, hipStream_t s);
 size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K);
+// Prefill GEMM. With a workspace of at least gemm_workspace_bytes(M, N, K) bytes whose
+// first gemm_arrival_words(M, N) words are zero, shapes that gain from it split K over
+// gemm_splits(M, N, K) workgroups per tile (the words are zero again afterwards);
+// otherwise (NULL or smaller workspace) one workgroup per tile.
+int gemm_splits(int64_t M, int64_t N, int64_t K);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int64_t gemm_arrival_words(int64_t M, int64_t N);
 hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
-                       const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
-                       hipStream_t s);
+                       const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *workspace,
+                       size_t workspace_bytes, hipStream_t s);
 
 }  // namespace bt

@@ -84,11 +84,20 @@ struct GemmCfg {
     static_assert((kWaves / 2) * 16 * 68 * 4 <= kStage, "epilogue slabs fit in two stages");
 };
 
-template <int BM, int BN, int WM, int WN, int NS, int WPE>
+// Split-K partial tile: the int32 accumulators of a BM x BN block.
+template <int BM, int BN>
+constexpr int kPartialBytes = BM * BN * 4;
+// Buffer-resource word 3 for raw (untyped) dword access on gfx9, and the cache-policy
+// operand of the buffer load / store builtins that selects sc1 (device coherence).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kSc1 = 1 << 4;
+
+template <int BM, int BN, int WM, int WN, int NS, int WPE, int SPLIT>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void k_gemm(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
     const float *__restrict__ sx, const int32_t *__restrict__ xsum, int64_t M, int64_t N, int KC, int NBLK,
-    int tiles_m, int tiles_n, int group, float *__restrict__ Y, int32_t *__restrict__ ACC, int vec)
+    int tiles_m, int tiles_n, int group, float *__restrict__ Y, int32_t *__restrict__ ACC, int vec,
+    char *__restrict__ partials, unsigned *__restrict__ arrivals, int per_xcd)
 {
     using C = GemmCfg<BM, BN, WM, WN, NS>;
     constexpr int TM = C::TM, TN = C::TN;
@@ -117,19 +126,26 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     const int wave = uniform(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
     const int g = lane >> 4, r = lane & 15;
-    const int nsteps = (KC + 1) / 2;  // 128-k steps (two 64-k chunks each)
-    const int last = nsteps - 1;
 
-    // Tile order. Workgroup b runs on XCD b % 8, and each XCD takes a contiguous run of
-    // a grouped tile list: groups of `group` token-tile rows, walked weight-tile column by
-    // column, so the workgroups resident on one XCD at a time cover a compact block of
-    // tiles whose activation and weight panels are shared in that XCD's L2.
+    // Work order. Workgroup b runs on XCD b % 8, and each XCD takes a contiguous run of
+    // per_xcd work items (a multiple of SPLIT): item = tile * SPLIT + split, so the splits
+    // of a tile run side by side on one XCD. Tiles follow a grouped list: groups of
+    // `group` token-tile rows, walked weight-tile column by column, so the workgroups
+    // resident on one XCD at a time cover a compact block of tiles whose activation and
+    // weight panels are shared in that XCD's L2.
     const int total = tiles_m * tiles_n;
-    const int per_xcd = (total + kXcds - 1) / kXcds;
     const int b = blockIdx.x;
-    const int t = (b % kXcds) * per_xcd + b / kXcds;
+    const int item = (b % kXcds) * per_xcd + b / kXcds;
+    const int t = item / SPLIT, split = item % SPLIT;
     if (t >= total)
         return;
+    // This split's 128-k steps: [step0, step0 + nsteps) of the tile's ceil(KC / 2).
+    const int nsteps_all = (KC + 1) / 2;
+    const int per_split = (nsteps_all + SPLIT - 1) / SPLIT;
+    const int step0 = min(split * per_split, nsteps_all);
+    const int nsteps = min(per_split, nsteps_all - step0);
+    const int last = nsteps - 1;
+    const int KCl = KC - 2 * step0;  // 64-k chunks from this split's first step on
     const int gsz = group * tiles_n;
     const int gid = t / gsz, gin = t - gid * gsz;
     const int gm0 = gid * group;
@@ -147,7 +163,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     // past K read the last chunk against zero activations (activation rows are
     // zero-padded to a multiple of 256 bytes).
     constexpr int NA = C::kAPerWave, NB = C::kBPerWave;
-    const int8_t *xbase = Xq + m0 * ldq;  // + st * 128 per step
+    const int8_t *xbase = Xq + m0 * ldq + (int64_t)step0 * kBK;  // + st * 128 per step
     uint32_t aoff[NA];
     int adst[NA];
 #pragma unroll
@@ -165,7 +181,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     for (int q = 0; q < NB; ++q) {
         const int blk = wave * NB + q;
         const int rbl = blk >> 1, gq = blk & 1;
-        wrow[q] = reinterpret_cast<const int8_t *>(Wp) + (int64_t)min(rb0 + rbl, NBLK - 1) * KC * 1024;
+        wrow[q] = reinterpret_cast<const int8_t *>(Wp) + (int64_t)min(rb0 + rbl, NBLK - 1) * KC * 1024 +
+                  (int64_t)step0 * 2048;
         bdst[q] = C::kABytes + blk * 1024;
         bchunk[q] = gq;
     }
@@ -177,7 +194,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
             __builtin_amdgcn_global_load_lds((global_void *)(xs + aoff[q]), (lds_void *)(sdst + adst[q]), 16, 0, 0);
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-            const int8_t *ws = wrow[q] + (int64_t)min(2 * st + bchunk[q], KC - 1) * 1024;
+            const int8_t *ws = wrow[q] + (int64_t)min(2 * st + bchunk[q], KCl - 1) * 1024;
             __builtin_amdgcn_global_load_lds((global_void *)(ws + boff), (lds_void *)(sdst + bdst[q]), 16, 0, 0);
         }
     };
@@ -297,6 +314,48 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
 
+    if constexpr (SPLIT > 1) {
+        // Split-K hand-off, with no workgroup ever waiting for another: every split stores
+        // its int32 partial tile (the MFMA layout, 16 bytes per lane per 16 x 16 tile) with
+        // device-coherent stores (sc1: visible to every XCD once performed, so no L2
+        // write-back fence is needed), waits until they are performed, then counts its
+        // arrival on the tile's counter. The split that arrives last adds the others'
+        // partials (device-coherent loads), returns the counter to zero for the next call
+        // and runs the epilogue; the others are done.
+        __shared__ unsigned arrived;
+        constexpr int kSlotBytes = kPartialBytes<BM, BN>;
+        const int lane_off = (wave * TM * TN * 64 + lane) * 16;
+        auto slot = [&](int sp) {
+            return __builtin_amdgcn_make_buffer_rsrc(partials + ((int64_t)t * SPLIT + sp) * kSlotBytes, (short)0,
+                                                     kSlotBytes, kBufferWord3);
+        };
+        const __amdgpu_buffer_rsrc_t mine = slot(split);
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+                __builtin_amdgcn_raw_buffer_store_b128(acc[a][i], mine, lane_off + (a * TN + i) * 1024, 0, kSc1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        if (tid == 0)
+            arrived = __hip_atomic_fetch_add(arrivals + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (arrived != SPLIT - 1)
+            return;
+        for (int sp = 0; sp < SPLIT; ++sp) {
+            if (sp == split)
+                continue;
+            const __amdgpu_buffer_rsrc_t other = slot(sp);
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int i = 0; i < TN; ++i)
+                    acc[a][i] += __builtin_amdgcn_raw_buffer_load_b128(other, lane_off + (a * TN + i) * 1024, 0, kSc1);
+        }
+        if (tid == 0)
+            arrivals[t] = 0u;
+    }
+
     // Epilogue: each wave passes its 64 x 64 accumulator tile through a private LDS
     // slab, 16 tokens at a time, so that stores are row-contiguous (16 bytes per lane
     // when vec, else 4), instead of the MFMA layout's 4-byte column fragments.
@@ -364,35 +423,79 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int WPE>
+template <int BM, int BN, int WM, int WN, int NS, int WPE, int SPLIT>
 hipError_t launch_t(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
-                    const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
+                    const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, char *partials,
+                    unsigned *arrivals, hipStream_t s)
 {
     using C = GemmCfg<BM, BN, WM, WN, NS>;
     const int KC = (int)((K + 63) / 64);
     const int NBLK = (int)((N + 63) / 64);
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
-    const int total = tiles_m * tiles_n;
-    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int items = tiles_m * tiles_n * SPLIT;
+    const int per_xcd = ((items + kXcds - 1) / kXcds + SPLIT - 1) / SPLIT * SPLIT;
     // 16-byte output stores need every row start 16-byte aligned.
     const int vec = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(acc) % 16 == 0);
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, WPE>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0, s,
-                       Wp, w_scale, Xq, ldq, sx, xsum, M, N, KC, NBLK, tiles_m, tiles_n, kGroup, Y, acc, vec);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, WPE, SPLIT>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0,
+                       s, Wp, w_scale, Xq, ldq, sx, xsum, M, N, KC, NBLK, tiles_m, tiles_n, kGroup, Y, acc, vec,
+                       partials, arrivals, per_xcd);
     return hipGetLastError();
 }
 
+constexpr int kBM = 64, kBN = 256;
+
+int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
+
 }  // namespace
 
+// Workgroups per output tile (each over a contiguous share of the k-steps). Measured on
+// the 2B-class prefill shapes: splitting pays when the tiles alone leave most of the
+// 768 workgroup slots (three per CU) empty and every split keeps enough steps to amortize
+// its prologue, epilogue and the partial-tile hand-off through memory.
+int gemm_splits(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t tiles = gemm_tiles(M, N);
+    const int64_t steps = ((K + 63) / 64 + 1) / 2;
+    const int64_t min_steps = tiles <= 128 ? 6 : 13;
+    for (int S = 4; S >= 2; --S)
+        if (tiles * S <= 768 && steps >= S * min_steps)
+            return S;
+    return 1;
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    const int S = gemm_splits(M, N, K);
+    if (S == 1)
+        return 0;
+    const int64_t tiles = gemm_tiles(M, N);
+    return (size_t)(round_up(4 * tiles, 256) + tiles * S * (int64_t)kPartialBytes<kBM, kBN>);
+}
+
 hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
-                       const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
+                       const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *workspace,
+                       size_t workspace_bytes, hipStream_t s)
 {
     // 64 x 256 blocks of 4 waves, three workgroups per CU (3-stage ring, 48 KB of LDS
     // each): with three waves per SIMD one wave's LDS reads, unpacking and barrier wait
     // hide under the others' MFMAs. Measured on the 2B-class prefill shapes against
-    // 128 x 256 blocks of 8 waves and against two workgroups per CU with a 4-stage ring.
-    return launch_t<64, 256, 1, 4, 3, 3>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    // 128 x 256 blocks of 8 waves, 64 x 128 blocks of 2 waves and two workgroups per CU
+    // with a 4-stage ring.
+    const int S = gemm_splits(M, N, K);
+    const size_t need = gemm_workspace_bytes(M, N, K);
+    if (S == 1 || !workspace || workspace_bytes < need)
+        return launch_t<kBM, kBN, 1, 4, 3, 3, 1>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, nullptr, nullptr, s);
+    unsigned *arrivals = static_cast<unsigned *>(workspace);
+    char *partials = static_cast<char *>(workspace) + round_up(4 * gemm_tiles(M, N), 256);
+    if (S == 2)
+        return launch_t<kBM, kBN, 1, 4, 3, 3, 2>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
+    if (S == 3)
+        return launch_t<kBM, kBN, 1, 4, 3, 3, 3>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
+    return launch_t<kBM, kBN, 1, 4, 3, 3, 4>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
 }
+
+int64_t gemm_arrival_words(int64_t M, int64_t N) { return gemm_tiles(M, N); }
 
 }  // namespace bt

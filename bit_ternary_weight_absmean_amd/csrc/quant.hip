@@ -42,14 +42,23 @@ __device__ inline int quant_one(float x, float inv)
     return (int)r;
 }
 
+// Zero-fill words [0, n) of `p`, spread over the whole grid (one store per word).
+__device__ inline void clear_words_strided(unsigned *p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+        p[i] = 0u;
+}
+
 __global__ __launch_bounds__(kThreads) void k_quant_act(const float *__restrict__ X, int64_t K, int64_t ldq,
                                                         int8_t *__restrict__ Xq, float *__restrict__ sx,
-                                                        int32_t *__restrict__ xsum)
+                                                        int32_t *__restrict__ xsum,
+    unsigned *__restrict__ clear, int64_t clear_words)
 {
     __shared__ float red_f[kThreads / 64];
     __shared__ int red_i[kThreads / 64];
     const int tid = threadIdx.x;
     const int64_t m = blockIdx.x;
+    clear_words_strided(clear, clear_words);
     const float *x = X + m * K;
     const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
 
@@ -119,12 +128,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(const float *__restrict_
 template <int C>
 __global__ __launch_bounds__(kThreads) void k_quant_act_reg(const float *__restrict__ X, int64_t K, int64_t ldq,
                                                             int8_t *__restrict__ Xq, float *__restrict__ sx,
-                                                            int32_t *__restrict__ xsum)
+                                                            int32_t *__restrict__ xsum,
+    unsigned *__restrict__ clear, int64_t clear_words)
 {
     __shared__ float red_f[kThreads / 64];
     __shared__ int red_i[kThreads / 64];
     const int tid = threadIdx.x;
     const int64_t m = blockIdx.x;
+    clear_words_strided(clear, clear_words);
     const float4 *x = reinterpret_cast<const float4 *>(X + m * K);
     const int nch = (int)(K >> 2);  // float4 chunks in the row (>= 1)
 
@@ -184,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_act_reg(const float *__restr
 }  // namespace
 
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int64_t ldq, int8_t *Xq, float *sx,
-                            int32_t *xsum, hipStream_t s)
+                            int32_t *xsum, unsigned *clear, int64_t clear_words, hipStream_t s)
 {
     if (M <= 0)
         return hipGetLastError();
@@ -192,19 +203,19 @@ hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int64_t ldq, i
     const bool reg = K > 0 && (K % 4) == 0 && (reinterpret_cast<uintptr_t>(X) % 16) == 0;
     const int64_t per_thread = (K / 4 + kThreads - 1) / kThreads;  // float4 chunks per thread
     if (reg && per_thread <= 1)
-        hipLaunchKernelGGL(k_quant_act_reg<1>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+        hipLaunchKernelGGL(k_quant_act_reg<1>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum, clear, clear_words);
     else if (reg && per_thread <= 2)
-        hipLaunchKernelGGL(k_quant_act_reg<2>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+        hipLaunchKernelGGL(k_quant_act_reg<2>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum, clear, clear_words);
     else if (reg && per_thread <= 4)
-        hipLaunchKernelGGL(k_quant_act_reg<4>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+        hipLaunchKernelGGL(k_quant_act_reg<4>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum, clear, clear_words);
     else if (reg && per_thread <= 8)
-        hipLaunchKernelGGL(k_quant_act_reg<8>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+        hipLaunchKernelGGL(k_quant_act_reg<8>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum, clear, clear_words);
     else if (reg && per_thread <= 16)
-        hipLaunchKernelGGL(k_quant_act_reg<16>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+        hipLaunchKernelGGL(k_quant_act_reg<16>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum, clear, clear_words);
     else if (reg && per_thread <= 32)
-        hipLaunchKernelGGL(k_quant_act_reg<32>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+        hipLaunchKernelGGL(k_quant_act_reg<32>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum, clear, clear_words);
     else
-        hipLaunchKernelGGL(k_quant_act, grid, block, 0, s, X, K, ldq, Xq, sx, xsum);
+        hipLaunchKernelGGL(k_quant_act, grid, block, 0, s, X, K, ldq, Xq, sx, xsum, clear, clear_words);
     return hipGetLastError();
 }
 

@@ -159,6 +159,30 @@ bt_status bt_ternary_gemm(const void *Wp, const float *w_scale, const int8_t *Xq
                           int64_t K, float *Y, int32_t *acc, void *stream);
 
 /*
+ * bt_ternary_gemm_ws -- bt_ternary_gemm with a caller workspace that lets shapes whose
+ * output tiles alone would leave most of the GPU idle (few tokens, or few output
+ * columns with long rows) split the k-range of every tile over several workgroups. The
+ * splits hand their int32 partial tiles over through the workspace and the last one to
+ * finish adds them up and runs the epilogue, so acc and Y are bit-identical to
+ * bt_ternary_gemm (integer partial sums, one scale multiply at the end). Follows the
+ * same passages as bt_ternary_gemm.
+ *   workspace        NULL (no split), or device memory of workspace_bytes bytes,
+ *                    256-byte aligned. The split route runs only when workspace_bytes >=
+ *                    bt_gemm_workspace_bytes(M, N, K) > 0; otherwise the call is
+ *                    bt_ternary_gemm.
+ *   Ownership        the caller owns the workspace. It must be zero-filled once before
+ *                    its first use (its leading words are per-tile arrival counters);
+ *                    every completed call leaves them zero again. Calls that share a
+ *                    workspace must not run concurrently.
+ * Errors are those of bt_ternary_gemm, plus BT_ERR_ALIGN for a misaligned workspace.
+ */
+size_t bt_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+bt_status bt_ternary_gemm_ws(const void *Wp, const float *w_scale, const int8_t *Xq,
+                             const float *x_scale, const int32_t *x_sum, int64_t M, int64_t N,
+                             int64_t K, float *Y, int32_t *acc, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
  * bt_ternary_linear -- the whole per-call path of the layer in one entry point:
  * fp32 activations in, fp32 outputs out (per-token absmax int8 quantization, the
  * integer ternary product and the scale epilogue). Follows the BitNet GPU guide,
@@ -169,7 +193,10 @@ bt_status bt_ternary_gemm(const void *Wp, const float *w_scale, const int8_t *Xq
  *   X          [M,K] fp32 row-major, 4-byte aligned.
  *   Y, acc     as for bt_ternary_gemv (either may be NULL, not both).
  *   workspace  bt_linear_workspace_bytes(M,N,K) bytes of device scratch, 256-byte
- *              aligned, or NULL when that size is 0.
+ *              aligned, or NULL when that size is 0. No initialization is needed: the
+ *              call writes every part it reads (for M > BT_GEMV_MAX_M it includes the
+ *              split-K workspace of bt_ternary_gemm_ws, whose counters the quantizer
+ *              launch zero-fills). Calls sharing a workspace must not overlap.
  * For M <= BT_GEMV_MAX_M and M * (K rounded up to 64) small enough for LDS the
  * quantizer runs inside the decode kernel (one launch, no workspace); otherwise the
  * call runs bt_quant_act into the workspace, then bt_ternary_gemv or

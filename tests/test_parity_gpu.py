@@ -254,6 +254,86 @@ def test_100b_down_decode_m16():
         np.testing.assert_array_equal(acc.cpu().numpy()[:, rows], acc_ref[:M])
 
 
+# Split-K route (bt_ternary_gemm_ws): shapes chosen so that the split heuristic picks
+# 4, 3 and 2 workgroups per tile, ragged in M, N and K.
+SPLIT_SHAPES = [(100, 2500, 6900, 4), (70, 600, 2500, 3), (65, 300, 1600, 2)]
+
+
+def split_of(M, N, K):
+    """Workgroups per tile the library picks, read back from the workspace size."""
+    n = bt.gemm_workspace_bytes(M, N, K)
+    if n == 0:
+        return 1
+    tiles = -(-M // 64) * -(-N // 256)
+    counters = -(-4 * tiles // 256) * 256
+    assert (n - counters) % (tiles * 64 * 256 * 4) == 0
+    return (n - counters) // (tiles * 64 * 256 * 4)
+
+
+def counters_zero(ws, M, N):
+    tiles = -(-M // 64) * -(-N // 256)
+    return bool((ws[: 4 * tiles].view(torch.int32) == 0).all())
+
+
+@pytest.mark.parametrize("M,N,K,S", SPLIT_SHAPES)
+def test_gemm_split_k(M, N, K, S):
+    note(f"gemm split-K M={M} N={N} K={K} S={S}")
+    assert split_of(M, N, K) == S
+    W = synth.gaussian((N, K), 9150 + N, 0.02)
+    X = synth.gaussian((M, K), 9650 + M)
+    ref = oracle_layer(W, X)
+    pw, q = gpu_pack(W), gpu_quant(X)
+    ws = bt.gemm_workspace(M, N, K, DEV)
+    for _ in range(2):  # the second call relies on the first leaving the counters at zero
+        check_product(pw, q, ref, M, N, bt.ternary_gemm, workspace=ws)
+        assert counters_zero(ws, M, N)
+    # bit-identical to the unsplit route
+    Y1, a1 = bt.ternary_gemm(pw, q, want_acc=True)
+    Y2, a2 = bt.ternary_gemm(pw, q, want_acc=True, workspace=ws)
+    np.testing.assert_array_equal(a1.cpu().numpy(), a2.cpu().numpy())
+    np.testing.assert_array_equal(f32_bits(Y1.cpu().numpy()), f32_bits(Y2.cpu().numpy()))
+
+
+def test_gemm_split_k_small_workspace_falls_back():
+    M, N, K = 100, 2500, 6900
+    note(f"gemm split-K short workspace M={M} N={N} K={K}")
+    W = synth.gaussian((N, K), 9151, 0.02)
+    X = synth.gaussian((M, K), 9651)
+    pw, q = gpu_pack(W), gpu_quant(X)
+    short = torch.zeros(bt.gemm_workspace_bytes(M, N, K) - 256, dtype=torch.uint8, device=DEV)
+    short.fill_(0xFF)  # never read: too small for the split route
+    Y1, a1 = bt.ternary_gemm(pw, q, want_acc=True)
+    Y2, a2 = bt.ternary_gemm(pw, q, want_acc=True, workspace=short)
+    np.testing.assert_array_equal(a1.cpu().numpy(), a2.cpu().numpy())
+    np.testing.assert_array_equal(f32_bits(Y1.cpu().numpy()), f32_bits(Y2.cpu().numpy()))
+
+
+@pytest.mark.parametrize("M,j", [(256, 0), (256, 1), (256, 3), (2048, 3)])
+def test_2b_prefill_split_shapes(M, j):
+    """The 2B prefill shapes that split (M=256: QKV, O, down; M=2048: down), in the
+    launch configuration the benchmark times: sampled rows against the oracle, every
+    output bit-identical to the unsplit route."""
+    name, N, K = synth.SHAPES_2B[j]
+    note(f"2B prefill split M={M} {name}")
+    assert split_of(M, N, K) > 1
+    W = synth.layer_weight(synth.CFG_2B_PREFILL, 0, j, N, K)
+    X = synth.layer_activation(synth.CFG_2B_PREFILL, j, M, K)
+    g = oracle.absmean(W)
+    T = oracle.ternarize(W, g)
+    Q, s, qs = oracle.quant_act(X)
+    rows = np.concatenate([np.arange(0, M, 37), [M - 1]])
+    acc_ref = oracle.ternary_matmul(T, Q[rows])
+    pw, q = gpu_pack(W), gpu_quant(X)
+    ws = bt.gemm_workspace(M, N, K, DEV)
+    Y, acc = bt.ternary_gemm(pw, q, want_acc=True, workspace=ws)
+    np.testing.assert_array_equal(acc.cpu().numpy()[rows], acc_ref)
+    assert tol_ok(Y.cpu().numpy()[rows], oracle.scale_epilogue(acc_ref, g, s[rows]))
+    Y1, a1 = bt.ternary_gemm(pw, q, want_acc=True)
+    np.testing.assert_array_equal(a1.cpu().numpy(), acc.cpu().numpy())
+    np.testing.assert_array_equal(f32_bits(Y1.cpu().numpy()), f32_bits(Y.cpu().numpy()))
+    assert counters_zero(ws, M, N)
+
+
 def test_2b_prefill_m2048_gate_up_sampled():
     note("2B prefill M=2048 gate_up")
     j = 2
@@ -388,6 +468,23 @@ def test_linear_workspace_routes(M, N, K):
     Y, acc = bt.linear(to_dev(X), gpu_pack(W), want_acc=True)
     np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
     assert tol_ok(Y.cpu().numpy(), ref["Y"])
+
+
+def test_linear_split_k_garbage_workspace():
+    """bt_ternary_linear on a shape whose GEMM splits K, with a workspace full of garbage:
+    the call initializes everything it reads (the quantizer zero-fills the counters)."""
+    M, N, K = 100, 2500, 6900
+    note(f"linear split-K garbage workspace M={M} N={N} K={K}")
+    assert split_of(M, N, K) == 4
+    W = synth.gaussian((N, K), 9152, 0.02)
+    X = synth.gaussian((M, K), 9652)
+    ref = oracle_layer(W, X)
+    pw = gpu_pack(W)
+    ws = torch.full((bt.linear_workspace_bytes(M, N, K),), 0xFF, dtype=torch.uint8, device=DEV)
+    for _ in range(2):
+        Y, acc = bt.linear(to_dev(X), pw, want_acc=True, workspace=ws)
+        np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+        assert tol_ok(Y.cpu().numpy(), ref["Y"])
 
 
 @pytest.mark.parametrize("j,name,N,K", [(j, *s) for j, s in enumerate(synth.SHAPES_2B)])
