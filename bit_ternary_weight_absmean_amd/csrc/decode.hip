@@ -479,12 +479,17 @@ int pick_rb(int64_t N)
 
 int pick_mt(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 
-// k-splits per 16-row block: enough waves to give every SIMD one (1024 waves).
+// k-splits per 16-row block: enough waves to give every SIMD one (1024 waves), two for
+// matrices of at most 512 row blocks (8192 rows): their rows are few, so each wave's share
+// of a long row is what keeps enough bytes in flight. Measured on the 2B, 7B and 100B
+// decode shapes at M = 1 (100B down 24.3 -> 17.3 us, 100B O 9.0 -> 7.0 us, 7B O and down
+// 10-15% faster, the rest unchanged).
 int pick_s(int64_t N)
 {
     const int64_t nb16 = (N + 15) / 16;
+    const int64_t target = nb16 <= 512 ? 2048 : 1024;
     int s = 1;
-    while (s < 8 && nb16 * s < 1024)
+    while (s < 8 && nb16 * s < target)
         s *= 2;
     return s;
 }
