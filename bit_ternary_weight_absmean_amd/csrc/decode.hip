@@ -15,7 +15,8 @@
 // load U of them per register batch (U * RB <= 8 uint4 per lane), one batch ahead.
 //
 // MFMA mapping (v_mfma_i32_16x16x64_i8, D = A * B): A = weights, 16 rows x 64 k;
-// B = tokens, 64 k x 16 columns (tokens m >= M are zero). For mask s the A dword j
+// B = tokens, 64 k x 16 columns (columns m >= M: zero in the direct kernel, a repeat of
+// token M - 1 in the fused one; either way never stored). For mask s the A dword j
 // of a lane is (word j & mask s): its byte e is the code of k = 64c + 16j + 4s + e
 // times 4^s (times 16 for s = 3). The matching B dword is bytes 16j + 4s .. +3 of
 // the lane's 64 activation bytes. Three accumulators (weights 1, 4, 16) recombine
@@ -30,7 +31,12 @@
 // so the quantizer only waits for the activations. It uses the arithmetic of
 // bt_quant_act (a = max |x|, inv = 127.0f / a, q = clamp(rint(x * inv), -127, 127),
 // s_x = a / 127.0f) and stages the int8 tokens in LDS (row pitch Kp + 16 bytes, so
-// the 16-byte operand reads of 16 tokens hit distinct banks).
+// the 16-byte operand reads of 16 tokens hit distinct banks, Kp = K rounded up to a whole
+// 256-k step, zero-filled). Within each 64-k chunk the quantizer stores the 4 x 4 dwords
+// transposed: bytes 16s .. 16s + 15 hold dwords s, s + 4, s + 8, s + 12 of the chunk, the
+// B operand of mask s, so each operand is one 16-byte LDS read with no register moves.
+// Slots outside the matrix need no masking there: weight chunks past K (clamped
+// duplicates) meet zero activations, and rows past N are never stored.
 #include "bt_internal.h"
 #include "wave.h"
 
@@ -90,6 +96,30 @@ __device__ inline uint4 mask_w(const v4i &w, bool keep)
     return make_uint4((uint32_t)((w[0] & k) | pad), (uint32_t)((w[1] & k) | pad), (uint32_t)((w[2] & k) | pad),
                       (uint32_t)((w[3] & k) | pad));
 }
+
+// One step, one row block, with the four B operands already in mask order (the fused
+// kernel's transposed LDS chunks): mfma_step<1> without the register transpose.
+__device__ inline void mfma_step_t(const v4i &w, const v4i (&b)[4], v4i &a1, v4i &a4, v4i &a16)
+{
+    v4i s0, s1, s2, s3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t pw = (uint32_t)w[j];
+        s0[j] = (int)(pw & kMask0);
+        s1[j] = (int)(pw & kMask1);
+        s2[j] = (int)(pw & kMask2);
+        s3[j] = (int)((pw >> 2) & kMask2);
+    }
+    a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(s0, b[0], a1, 0, 0, 0);
+    a4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(s1, b[1], a4, 0, 0, 0);
+    a16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(s2, b[2], a16, 0, 0, 0);
+    a16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(s3, b[3], a16, 0, 0, 0);
+}
+
+// Byte offset, within an LDS token row, of the activation dword k4 (k = 4 k4 .. + 3):
+// chunk k4 / 16, transposed inside the chunk (dword d = k4 % 16 goes to 16 (d % 4) +
+// 4 (d / 4)).
+__device__ inline int lds_x_offset(int k4) { return (k4 >> 4) * 64 + 16 * (k4 & 3) + 4 * ((k4 >> 2) & 3); }
 
 __device__ inline void unpack16(const uint4 (&v)[4], int32_t (&xw)[16])
 {
@@ -231,7 +261,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     int *s_qpart = reinterpret_cast<int *>(s_apart + WAVES * kMaxM);   // [WAVES][kMaxM]
     int *red = s_qpart + WAVES * kMaxM;                                // [WAVES][4][64] (S > 1)
     int8_t *xq = reinterpret_cast<int8_t *>(red + (S > 1 ? WAVES * 256 : 0));
-    const int pitch = KC * 64 + kPitchPad;
+    const int KC4 = (KC + 3) & ~3;  // chunks in whole 256-k steps (zero-filled past KC)
+    const int pitch = KC4 * 64 + kPitchPad;
 
     const float gamma = w_scale[0];  // issued first: the epilogue needs it last
     const int tid = threadIdx.x;
@@ -354,15 +385,15 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
 #pragma unroll
                 for (int i = 0; i < RPT; ++i) {
                     const int k4 = tid + i * T;
-                    if (k4 < KC * 16) {
+                    if (k4 < KC4 * 16) {
                         const uint32_t p = (k4 < K4) ? quant_pack4(xr[m][i], inv) : 0u;
                         sum += sum_bytes_s8(p);
-                        *reinterpret_cast<uint32_t *>(qrow + 4 * k4) = p;
+                        *reinterpret_cast<uint32_t *>(qrow + lds_x_offset(k4)) = p;
                     }
                 }
                 // zero padding past the register-held part of the row
-                for (int k4 = tid + RPT * T; k4 < KC * 16; k4 += T)
-                    *reinterpret_cast<uint32_t *>(qrow + 4 * k4) = 0u;
+                for (int k4 = tid + RPT * T; k4 < KC4 * 16; k4 += T)
+                    *reinterpret_cast<uint32_t *>(qrow + lds_x_offset(k4)) = 0u;
                 sum = wave_sum_i32(sum);
                 if (lane == 0)
                     s_qpart[wave * kMaxM + m] = sum;
@@ -377,10 +408,10 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
             int8_t *qrow = xq + m * pitch;
             const float *xm = X + (int64_t)m * K;
             int sum = 0;
-            for (int k4 = tid; k4 < KC * 16; k4 += T) {
+            for (int k4 = tid; k4 < KC4 * 16; k4 += T) {
                 const uint32_t p = (k4 < K4) ? quant_pack4(load4(xm, k4), inv) : 0u;
                 sum += sum_bytes_s8(p);
-                *reinterpret_cast<uint32_t *>(qrow + 4 * k4) = p;
+                *reinterpret_cast<uint32_t *>(qrow + lds_x_offset(k4)) = p;
             }
             sum = wave_sum_i32(sum);
             if (lane == 0)
@@ -397,19 +428,12 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
         for (int u = 0; u < U; ++u) {
             const int i = b * U + u;
             if (i < nmine) {
+                // c < 4 * nsteps <= KC4: inside the zero-filled row. Token columns
+                // r >= M read token M - 1 (their outputs are never stored).
                 const int c = 4 * (ks + S * i) + g;
-                uint4 xv[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
-                               make_uint4(0, 0, 0, 0)};
-                if (r < M && c < KC) {
-                    const uint4 *p = reinterpret_cast<const uint4 *>(xq + r * pitch + c * 64);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        xv[q] = p[q];
-                }
-                int32_t xw[16];
-                unpack16(xv, xw);
-                const uint4 wk[1] = {mask_w(w[u], c < KC && b16 < NB16)};
-                mfma_step<1>(wk, xw, a1, a4, a16);
+                const v4i *p = reinterpret_cast<const v4i *>(xq + min(r, M - 1) * pitch + c * 64);
+                const v4i b[4] = {p[0], p[1], p[2], p[3]};
+                mfma_step_t(w[u], b, a1[0], a4[0], a16[0]);
             }
         }
     };
@@ -497,7 +521,8 @@ int pick_s(int64_t N)
 size_t fused_lds(int64_t M, int64_t K, int s)
 {
     const int64_t KC = (K + 63) / 64;
-    return 2 * kFusedWaves * kMaxM * 4 + (s > 1 ? kFusedWaves * 256 * 4 : 0) + (size_t)M * (KC * 64 + kPitchPad);
+    const int64_t KC4 = (KC + 3) / 4 * 4;
+    return 2 * kFusedWaves * kMaxM * 4 + (s > 1 ? kFusedWaves * 256 * 4 : 0) + (size_t)M * (KC4 * 64 + kPitchPad);
 }
 
 template <int MT, int S, int RX, int U>
