@@ -51,7 +51,7 @@ hipError_t launch_gemv_dot4(const uint4 *Wp, const float *w_scale, const int8_t 
 hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq,
                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
                             int32_t *acc, hipStream_t s);
-// Fused decode (quantize + product + epilogue) for M <= 16; LDS bytes it needs.
+// Fused decode (quantize + product + epilogue) for M <= 4; LDS bytes it needs.
 hipError_t launch_linear_decode(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N,
                                 int64_t K, float *Y, int32_t *acc, hipStream_t s);
 size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K);

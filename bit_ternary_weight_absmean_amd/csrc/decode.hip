@@ -1,5 +1,6 @@
-// Decode product on int8 MFMA for 1 <= M <= 16 tokens, optionally with the per-token
-// activation quantizer fused in (fp32 x in, fp32 y out: one launch per linear layer).
+// Decode product on int8 MFMA for 1 <= M <= 16 tokens (pre-quantized activations), and for
+// M <= 4 also with the per-token activation quantizer fused in (fp32 x in, fp32 y out: one
+// launch per linear layer).
 //
 // "bit-floor" page, "The core math": integer inner loop, one scale multiply at the
 // end; "BitCompute" page, "Features": ternary weights make the product add /
@@ -79,9 +80,11 @@ __device__ inline void mfma_step(const uint4 (&w)[RB], const int32_t (&xw)[16], 
 }
 
 // Weight uint4 of block b16, chunk c, lane row r, from a clamped, always valid address
-// (callers load only with KC >= 1). Slots outside the matrix get padding words where
-// the value is used (mask_w), not here: a select or a branch right after a load makes
-// the compiler wait for that load before it issues the next one.
+// (callers load only with KC >= 1). Slots outside the matrix are not masked here: a
+// select or a branch right after a load would make the compiler wait for that load before
+// the next one. k_gemv_direct masks them where the values are used (mask_w); the other
+// kernels need no mask, because chunks past K meet zero activations there and rows past
+// N are never stored.
 __device__ inline v4i load_w_raw(const uint4 *__restrict__ Wp, int b16, int NB16, int c, int KC, int r)
 {
     const int bb = min(b16, NB16 - 1), cc = min(max(c, 0), KC - 1);
@@ -95,6 +98,17 @@ __device__ inline uint4 mask_w(const v4i &w, bool keep)
     const int pad = (int)kPadWord & ~k;
     return make_uint4((uint32_t)((w[0] & k) | pad), (uint32_t)((w[1] & k) | pad), (uint32_t)((w[2] & k) | pad),
                       (uint32_t)((w[3] & k) | pad));
+}
+
+__device__ inline void unpack16(const uint4 (&v)[4], int32_t (&xw)[16])
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        xw[4 * q + 0] = (int32_t)v[q].x;
+        xw[4 * q + 1] = (int32_t)v[q].y;
+        xw[4 * q + 2] = (int32_t)v[q].z;
+        xw[4 * q + 3] = (int32_t)v[q].w;
+    }
 }
 
 // One step, one row block, with the four B operands already in mask order (the fused
@@ -120,17 +134,6 @@ __device__ inline void mfma_step_t(const v4i &w, const v4i (&b)[4], v4i &a1, v4i
 // chunk k4 / 16, transposed inside the chunk (dword d = k4 % 16 goes to 16 (d % 4) +
 // 4 (d / 4)).
 __device__ inline int lds_x_offset(int k4) { return (k4 >> 4) * 64 + 16 * (k4 & 3) + 4 * ((k4 >> 2) & 3); }
-
-__device__ inline void unpack16(const uint4 (&v)[4], int32_t (&xw)[16])
-{
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        xw[4 * q + 0] = (int32_t)v[q].x;
-        xw[4 * q + 1] = (int32_t)v[q].y;
-        xw[4 * q + 2] = (int32_t)v[q].z;
-        xw[4 * q + 3] = (int32_t)v[q].w;
-    }
-}
 
 // Partial accumulators of all waves -> y and acc. red[w][k][v][lane]; o = m * rows + nl.
 // token_stats(m, qs, sx) supplies sum_k q and s_x of token m.
@@ -162,8 +165,10 @@ __device__ inline void epilogue(const int *red, int tid, int M, int64_t N, float
     }
 }
 
-// ------------------------------------------------------------ direct kernel
+// ------------------------------------------------------------ direct kernels
 // Pre-quantized int8 activations read straight from global memory (L2) per step.
+// k_gemv_direct (two or four row blocks per workgroup): one batch of U = 2 steps at a
+// time, masks where the values are used. k_gemv_direct_db (one row block): see below.
 template <int RB>
 __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
@@ -220,6 +225,100 @@ __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct(
             for (int k = 0; k < RB; ++k)
                 wm[k] = mask_w(w[u][k], c < KC && blockIdx.x * RB + k < NB16);
             mfma_step<RB>(wm, xw, a1, a4, a16);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < RB; ++k)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            red[((wave * RB + k) * 4 + v) * 64 + lane] = a1[k][v] + (a4[k][v] >> 2) + (a16[k][v] >> 4);
+    __syncthreads();
+    epilogue<WAVES, RB>(red, tid, M, N, w_scale[0],
+                        [&](int m, int &qs, float &sxm) {
+                            qs = xsum_in[m];
+                            sxm = sx_in[m];
+                        },
+                        Y, ACC);
+}
+
+// k_gemv_direct_db: wave w of the workgroup takes steps w, w + 4, ... of the workgroup's
+// RB row blocks, U steps per register batch, two batches in flight (as in the fused
+// kernel: measured faster with one row block per workgroup, e.g. 7B down at M = 8 9.9 ->
+// 7.8 us). Every load is issued
+// raw at a clamped address and nothing is masked: activation chunks past K come from the
+// zero padding of the Xq rows (bt_act_row_bytes(K) bytes: whole 256-k steps), so weight
+// chunks past K (clamped duplicates) meet zeros; token columns r >= M re-read token
+// M - 1 and rows past N are never stored.
+template <int RB, int U>
+__global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct_db(
+    const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
+    const float *__restrict__ sx_in, const int32_t *__restrict__ xsum_in, int M, int64_t N, int KC, int NB16,
+    float *__restrict__ Y, int32_t *__restrict__ ACC)
+{
+    constexpr int WAVES = kDirectWaves;
+    __shared__ int red[WAVES * RB * 256];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int g = lane >> 4;
+    const int r = lane & 15;
+    const int nsteps = (KC + 3) >> 2;
+    const int nmine = (wave < nsteps) ? (nsteps - 1 - wave) / WAVES + 1 : 0;
+    const int nb = (nmine + U - 1) / U;
+    const int8_t *xrow = Xq + (int64_t)min(r, M - 1) * ldq;
+    const int cmax = 4 * nsteps - 1;  // last 64-k chunk of the zero-padded activation row
+
+    v4i a1[RB], a4[RB], a16[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k)
+        a1[k] = a4[k] = a16[k] = v4i{0, 0, 0, 0};
+
+    v4i w0[U][RB], x0[U][4], w1[U][RB], x1[U][4];
+    auto load_batch = [&](auto &w, auto &x, int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = 4 * (wave + WAVES * (b * U + u)) + g;
+#pragma unroll
+            for (int k = 0; k < RB; ++k)
+                w[u][k] = load_w_raw(Wp, blockIdx.x * RB + k, NB16, c, KC, r);
+            const v4i *p = reinterpret_cast<const v4i *>(xrow + (int64_t)min(c, cmax) * 64);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                x[u][q] = p[q];
+        }
+    };
+    auto compute_batch = [&](const auto &w, const auto &x, int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (b * U + u < nmine) {
+                int32_t xw[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        xw[4 * q + d] = x[u][q][d];
+                uint4 wk[RB];
+#pragma unroll
+                for (int k = 0; k < RB; ++k)
+                    wk[k] = make_uint4((uint32_t)w[u][k][0], (uint32_t)w[u][k][1], (uint32_t)w[u][k][2],
+                                       (uint32_t)w[u][k][3]);
+                mfma_step<RB>(wk, xw, a1, a4, a16);
+            }
+        }
+    };
+    // K = 0 (nsteps = 0): no loads at all (the operand pointers may be null).
+    if (nsteps > 0) {
+        load_batch(w0, x0, 0);
+        load_batch(w1, x1, 1);
+    }
+    for (int b = 0; b < nb; b += 2) {
+        compute_batch(w0, x0, b);
+        if (b + 2 < nb)
+            load_batch(w0, x0, b + 2);
+        if (b + 1 < nb) {
+            compute_batch(w1, x1, b + 1);
+            if (b + 3 < nb)
+                load_batch(w1, x1, b + 3);
         }
     }
 #pragma unroll
@@ -501,7 +600,9 @@ int pick_rb(int64_t N)
     return 1;
 }
 
-int pick_mt(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+// Token capacity of the fused kernel (it takes M <= 4: past that one quantizer launch
+// and the direct kernel are faster).
+int pick_mt(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
 
 // k-splits per 16-row block: enough waves to give every SIMD one (1024 waves), two for
 // matrices of at most 512 row blocks (8192 rows): their rows are few, so each wave's share
@@ -596,8 +697,19 @@ hipError_t launch_direct_t(const uint4 *Wp, const float *w_scale, const int8_t *
     const int KC = (int)((K + 63) / 64);
     const int NB16 = (int)(((N + 63) / 64) * 4);
     const int64_t nb16 = (N + 15) / 16;
-    hipLaunchKernelGGL((k_gemv_direct<RB>), dim3((unsigned)((nb16 + RB - 1) / RB)), dim3(kDirectWaves * 64), 0, s,
-                       Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, NB16, Y, acc);
+    const dim3 grid((unsigned)((nb16 + RB - 1) / RB)), block(kDirectWaves * 64);
+    // One row block: two-step batches, two in flight once a wave owns more than two steps.
+    // More row blocks: the single-batch kernel (measured faster there: more waves resident).
+    const int64_t mine = ((K + 255) / 256 + kDirectWaves - 1) / kDirectWaves;
+    if (RB > 1)
+        hipLaunchKernelGGL((k_gemv_direct<RB>), grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, NB16, Y,
+                           acc);
+    else if (mine <= 2)
+        hipLaunchKernelGGL((k_gemv_direct_db<RB, 1>), grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M,
+                           N, KC, NB16, Y, acc);
+    else
+        hipLaunchKernelGGL((k_gemv_direct_db<RB, 2>), grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M,
+                           N, KC, NB16, Y, acc);
     return hipGetLastError();
 }
 
@@ -619,12 +731,12 @@ hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, const int8_t 
 hipError_t launch_linear_decode(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N,
                                 int64_t K, float *Y, int32_t *acc, hipStream_t s)
 {
+    if (M > 4)
+        return hipErrorInvalidValue;
     switch (pick_mt(M)) {
     case 1: return launch_fused_mt<1>(Wp, w_scale, X, M, N, K, Y, acc, s);
     case 2: return launch_fused_mt<2>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    case 4: return launch_fused_mt<4>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    case 8: return launch_fused_mt<8>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    default: return launch_fused_mt<16>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    default: return launch_fused_mt<4>(Wp, w_scale, X, M, N, K, Y, acc, s);
     }
 }
 

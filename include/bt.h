@@ -197,8 +197,8 @@ bt_status bt_ternary_gemm_ws(const void *Wp, const float *w_scale, const int8_t 
  *              call writes every part it reads (for M > BT_GEMV_MAX_M it includes the
  *              split-K workspace of bt_ternary_gemm_ws, whose counters the quantizer
  *              launch zero-fills). Calls sharing a workspace must not overlap.
- * For M <= BT_GEMV_MAX_M and M * (K rounded up to 64) small enough for LDS the
- * quantizer runs inside the decode kernel (one launch, no workspace); otherwise the
+ * For M <= 4 tokens with M * K <= 32768 the quantizer runs inside the decode kernel
+ * (one launch, no workspace); otherwise the
  * call runs bt_quant_act into the workspace, then bt_ternary_gemv or
  * bt_ternary_gemm. Both routes give results bit-identical to calling bt_quant_act
  * and bt_ternary_gemv / bt_ternary_gemm yourself.

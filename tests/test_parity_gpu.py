@@ -433,8 +433,10 @@ def test_side_stream_and_graph_replay():
 
 
 # ------------------------------------------------- fused linear entry point
-LINEAR_CASES = [(1, 1, 1), (1, 100, 300), (2, 130, 129), (3, 65, 1000), (5, 200, 700), (8, 64, 64),
-                (16, 300, 517), (16, 1000, 2560), (1, 2560, 6912), (8, 4096, 4096)]
+# Shapes the fused kernel takes (M <= 4 and M * K <= 32768), token counts 1, 2 and 4
+# (the kernel's three token capacities), ragged and aligned K.
+LINEAR_CASES = [(1, 1, 1), (1, 100, 300), (2, 130, 129), (3, 65, 1000), (4, 200, 700), (4, 64, 64),
+                (4, 300, 517), (4, 1000, 2560), (1, 2560, 6912), (1, 600, 28672), (4, 4096, 8192)]
 
 
 @pytest.mark.parametrize("M,N,K", LINEAR_CASES)
@@ -457,9 +459,12 @@ def test_linear_fused(M, N, K):
     np.testing.assert_array_equal(Y.cpu().numpy(), Ys.cpu().numpy())
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 512, 8192), (16, 600, 28672), (40, 300, 700), (300, 257, 1000)])
+@pytest.mark.parametrize("M,N,K", [(16, 512, 8192), (16, 600, 28672), (40, 300, 700), (300, 257, 1000),
+                                   (5, 200, 700), (8, 64, 64), (16, 300, 517), (16, 1000, 2560),
+                                   (8, 4096, 4096), (4, 300, 11008)])
 def test_linear_workspace_routes(M, N, K):
-    """Shapes past the fused kernel's LDS budget (and M > 16) go through the workspace route."""
+    """Shapes outside the fused kernel's range (M > 4, M * K > 32768, M > 16) go through the
+    workspace route: bt_quant_act, then bt_ternary_gemv or bt_ternary_gemm."""
     note(f"linear route M={M} N={N} K={K}")
     assert bt.linear_workspace_bytes(M, N, K) > 0
     W = synth.gaussian((N, K), 9300 + N, 0.02)
