@@ -154,6 +154,24 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     const int64_t m0 = (int64_t)tm * BM;
     const int rb0 = tn * (BN / 64);  // first 64-row weight block of the workgroup
 
+    // The epilogue's inputs, requested now so that their round trip overlaps the main loop
+    // instead of following it: gamma, and the row statistics of the workgroup's BM rows
+    // (thread t holds row m0 + t % BM, clamped; every thread loads, so the loads need no
+    // branch). The first BM threads park them in LDS once the prologue's wait has retired
+    // them (they are older than every operand load).
+    __shared__ int32_t s_xsum[BM];
+    __shared__ float s_sx[BM];
+    const float gamma = w_scale[0];
+    const int64_t m_stat = min(m0 + tid % BM, M - 1);
+    const int32_t xsum_t = xsum[m_stat];
+    const float sx_t = sx[m_stat];
+    auto park_stats = [&] {
+        if (tid < BM) {
+            s_xsum[tid] = xsum_t;
+            s_sx[tid] = sx_t;
+        }
+    };
+
     // This wave's direct-load blocks per step. Activation block (16-row tile at, half h):
     // lane L brings row 16 at + 8 h + L / 8, the piece that slot L % 8 of that row holds
     // (slot ^ row ^ h). Weight block (64-row block rbl, chunk gq of the step): lane L
@@ -288,6 +306,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
             issue(min(3, last), lds3);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * C::kBlocksPerWave));
         barrier();
+        park_stats();
         read_a(lds0, a_off0, fa0);
         read_b(lds0, fb);
         // Steps in groups of NS (step st uses stage st % NS), then the remainder.
@@ -308,6 +327,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
             if (st + 2 < nsteps)
                 step(I2{}, st + 2);
         }
+    } else {
+        park_stats();
     }
     // Retire the trailing (clamped, unused) loads, then wait until every wave is done
     // with the stages: the epilogue reuses their LDS.
@@ -365,16 +386,15 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     // (the first half of the waves in stage 0's memory, the second half in stage 1's)
     constexpr int kHalf = C::kWaves / 2;
     int32_t *slab = reinterpret_cast<int32_t *>(wave < kHalf ? lds0 : lds1) + (wave % kHalf) * 16 * kPitchW;
-    const float gamma = w_scale[0];
     const int64_t n0 = (int64_t)tn * BN + wn * 64;
-    // Row statistics of the lane's 16 rows in one batch (clamped rows): one round trip.
+    // Row statistics of the lane's 16 rows, from LDS.
     int32_t xs_r[TM * 4];
     float sx_r[TM * 4];
 #pragma unroll
     for (int c = 0; c < TM * 4; ++c) {
-        const int64_t m = min(m0 + wm * 64 + (c >> 2) * 16 + 4 * (c & 3) + g, M - 1);
-        xs_r[c] = xsum[m];
-        sx_r[c] = sx[m];
+        const int row = wm * 64 + (c >> 2) * 16 + 4 * (c & 3) + g;
+        xs_r[c] = s_xsum[row];
+        sx_r[c] = s_sx[row];
     }
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
