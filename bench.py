@@ -32,6 +32,7 @@ reported only while the kernel sources still hash to the values recorded there.
 from __future__ import annotations
 
 import argparse
+import collections
 import csv
 import glob
 import hashlib
@@ -72,7 +73,10 @@ def parse():
                                                         "OUT_JSON"),
                    help="write a traffic summary from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs of this "
                         "workload and of --calib-copy, for the workload's dominant kernel")
-    p.add_argument("--command", default="", help="the rocprofv3 command line recorded with --summarize-pmc")
+    p.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "OUT_JSON"),
+                   help="write an MFMA-utilization summary for the prefill GEMM from a rocprofv3 --pmc "
+                        "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_I8 run of this workload")
+    p.add_argument("--command", default="", help="the rocprofv3 command line recorded with --summarize-pmc / -mfma")
     return p.parse_args()
 
 
@@ -356,6 +360,68 @@ def summarize_pmc(args):
     print(json.dumps(out))
 
 
+def summarize_mfma(args):
+    """Per-dispatch MFMA utilization of k_gemm: rocprofv3's MfmaUtil (MFMA-busy cycles of all SIMDs over
+    GPU-active cycles times the SIMD count, i.e. measured at the clock the chip actually ran) and the int8
+    MFMA op count (SQ_INSTS_VALU_MFMA_MOPS_I8, units of 512 ops) against the algorithmic 2*M*N*K."""
+    pmc_dir, out_json = args.summarize_mfma
+    spec = workload_spec(args.workload, args.m)
+    if not spec["prefill"]:
+        raise SystemExit("--summarize-mfma is for the prefill workload")
+    kernel = "k_gemm"
+    util = [float(r["Counter_Value"]) for r in _pmc_rows(pmc_dir, "MfmaUtil") if kernel in r["Kernel_Name"]]
+    mops = [float(r["Counter_Value"]) for r in _pmc_rows(pmc_dir, "SQ_INSTS_VALU_MFMA_MOPS_I8")
+            if kernel in r["Kernel_Name"]]
+    if not util or not mops:
+        raise SystemExit(f"no MfmaUtil / SQ_INSTS_VALU_MFMA_MOPS_I8 rows for {kernel} in {pmc_dir}")
+    M = spec["M"]
+    alg_ops = [2 * M * N * K for _, N, K in spec["shapes"]]
+    # per matrix shape (identified by its exact op count), with the dispatch durations of the
+    # counter run itself
+    shape_of = {2 * M * N * K: f"{n} {N}x{K}" for n, N, K in spec["shapes"]}
+    per = collections.defaultdict(lambda: {"util": [], "ops": [], "us": []})
+    util_rows = [r for r in _pmc_rows(pmc_dir, "MfmaUtil") if kernel in r["Kernel_Name"]]
+    mops_rows = {r["Dispatch_Id"]: float(r["Counter_Value"]) for r in _pmc_rows(pmc_dir, "SQ_INSTS_VALU_MFMA_MOPS_I8")
+                 if kernel in r["Kernel_Name"]}
+    for r in util_rows:
+        ops = 512 * mops_rows.get(r["Dispatch_Id"], 0.0)
+        key = shape_of.get(round(ops), f"grid {r['Grid_Size']}")
+        per[key]["util"].append(float(r["Counter_Value"]))
+        per[key]["ops"].append(ops)
+        per[key]["us"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    per_shape = {k: {"launches": len(v["util"]), "mfma_util_percent": round(sum(v["util"]) / len(v["util"]), 2),
+                     "dispatch_us_under_counters": round(sum(v["us"]) / len(v["us"]), 2),
+                     "TOPS_under_counters": round(sum(v["ops"]) / sum(v["us"]) / 1e6, 1)}
+                 for k, v in per.items()}
+    out = {
+        "kernel": kernel, "workload": spec["desc"], "M": M,
+        "source_sha256": source_hash(kernel),
+        "launches_counted": len(util),
+        "per_shape": per_shape,
+        "mfma_util_percent_mean": round(sum(util) / len(util), 2),
+        "mfma_util_percent_min": round(min(util), 2), "mfma_util_percent_max": round(max(util), 2),
+        "int8_mfma_ops_per_launch": round(512 * sum(mops) / len(mops)),
+        "algorithmic_ops_per_launch": round(sum(alg_ops) / len(alg_ops)),
+        "command": args.command,
+    }
+    with open(out_json, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
+def mfma_util_for(spec, kernel):
+    """Mean MfmaUtil (%) from the committed counter summary, while the kernel sources still match."""
+    path = os.path.join(ROOT, "profiles", f"mfma_{kernel}_{spec['name']}_m{spec['M']}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != source_hash(kernel):
+        return None
+    return rec["mfma_util_percent_mean"]
+
+
 def traffic_for(spec, kernel):
     path = traffic_path(spec["name"], kernel, spec["M"])
     if not os.path.exists(path):
@@ -377,6 +443,9 @@ def main():
         return 2
     if args.summarize_pmc:
         summarize_pmc(args)
+        return 0
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return 0
     if args.calib_copy:
         calib_copy()
@@ -430,7 +499,8 @@ def main():
                    "step_TOPS": round(g["step_ops"] / (g["ms_step"] * 1e-3) / 1e12, 3),
                    "weights_per_s": round(sum(N * K for _, N, K in spec["shapes"]) * spec["layers"] /
                                           (g["ms_step"] * 1e-3), 1),
-                   "setup_s": round(g["setup_s"], 1)},
+                   "setup_s": round(g["setup_s"], 1),
+                   "mfma_util_percent_counters": mfma_util_for(spec, g["kernel"]) if spec["prefill"] else None},
     }
     print(json.dumps(line), flush=True)
     return 0
