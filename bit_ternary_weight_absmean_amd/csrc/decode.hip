@@ -485,8 +485,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
                 for (int i = 0; i < RPT; ++i) {
                     const int k4 = tid + i * T;
                     if (k4 < KC4 * 16) {
-                        const uint32_t p = (k4 < K4) ? quant_pack4(xr[m][i], inv) : 0u;
-                        sum += sum_bytes_s8(p);
+                        // xr is zero past K (masked at load): those dwords quantize to 0
+                        const uint32_t p = quant_pack4_sum(xr[m][i], inv, sum);
                         *reinterpret_cast<uint32_t *>(qrow + lds_x_offset(k4)) = p;
                     }
                 }
@@ -508,8 +508,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
             const float *xm = X + (int64_t)m * K;
             int sum = 0;
             for (int k4 = tid; k4 < KC4 * 16; k4 += T) {
-                const uint32_t p = (k4 < K4) ? quant_pack4(load4(xm, k4), inv) : 0u;
-                sum += sum_bytes_s8(p);
+                const uint32_t p = (k4 < K4) ? quant_pack4_sum(load4(xm, k4), inv, sum) : 0u;
                 *reinterpret_cast<uint32_t *>(qrow + lds_x_offset(k4)) = p;
             }
             sum = wave_sum_i32(sum);

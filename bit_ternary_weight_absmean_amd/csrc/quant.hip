@@ -10,9 +10,11 @@
 //
 // Per row m: a = max_k |x| (exact, order-free), inv = 127.0f / a (IEEE fp32
 // division, correctly rounded), q = clamp(rint(x * inv), -127, 127) (round half to
-// even), s_x = a / 127.0f and sum_k q. The int8 row is written with stride ldq
+// even; computed by quant_pack4_sum, which needs no clamp), s_x = a / 127.0f and
+// sum_k q. The int8 row is written with stride ldq
 // (K rounded up to 256) and zero padding, four codes per 32-bit store.
 #include "bt_internal.h"
+#include "wave.h"
 
 namespace bt {
 namespace {
@@ -33,13 +35,6 @@ __device__ inline int wave_sum(int v)
     for (int off = 32; off > 0; off >>= 1)
         v += __shfl_xor(v, off);
     return v;
-}
-
-__device__ inline int quant_one(float x, float inv)
-{
-    float r = rintf(x * inv);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
 }
 
 // Zero-fill words [0, n) of `p`, spread over the whole grid (one store per word).
@@ -88,25 +83,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(const float *__restrict_
     int8_t *q = Xq + m * ldq;
     int sum = 0;
     for (int64_t k = 4 * tid; k < ldq; k += 4 * kThreads) {
-        int e0 = 0, e1 = 0, e2 = 0, e3 = 0;
-        if (!zero) {
-            if (vec && k + 4 <= K) {
-                const float4 v = *reinterpret_cast<const float4 *>(x + k);
-                e0 = quant_one(v.x, inv);
-                e1 = quant_one(v.y, inv);
-                e2 = quant_one(v.z, inv);
-                e3 = quant_one(v.w, inv);
-            } else {
-                if (k + 0 < K) e0 = quant_one(x[k + 0], inv);
-                if (k + 1 < K) e1 = quant_one(x[k + 1], inv);
-                if (k + 2 < K) e2 = quant_one(x[k + 2], inv);
-                if (k + 3 < K) e3 = quant_one(x[k + 3], inv);
-            }
+        // Values past K (and every value of an all-zero row, inv = 0) quantize to 0.
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (vec && k + 4 <= K) {
+            v = *reinterpret_cast<const float4 *>(x + k);
+        } else {
+            if (k + 0 < K) v.x = x[k + 0];
+            if (k + 1 < K) v.y = x[k + 1];
+            if (k + 2 < K) v.z = x[k + 2];
+            if (k + 3 < K) v.w = x[k + 3];
         }
-        sum += e0 + e1 + e2 + e3;
-        const uint32_t packed = (uint32_t)(e0 & 0xff) | ((uint32_t)(e1 & 0xff) << 8) |
-                                ((uint32_t)(e2 & 0xff) << 16) | ((uint32_t)(e3 & 0xff) << 24);
-        *reinterpret_cast<uint32_t *>(q + k) = packed;
+        *reinterpret_cast<uint32_t *>(q + k) = quant_pack4_sum(v, inv, sum);
     }
     sum = wave_sum(sum);
     if ((tid & 63) == 0)
@@ -168,12 +155,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_act_reg(const float *__restr
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int idx = tid + c * kThreads;
-        const int e0 = quant_one(v[c].x, inv), e1 = quant_one(v[c].y, inv);
-        const int e2 = quant_one(v[c].z, inv), e3 = quant_one(v[c].w, inv);
-        sum += e0 + e1 + e2 + e3;
+        // chunks past the row were loaded as zeros: they add 0 to the sum
+        const uint32_t packed = quant_pack4_sum(v[c], inv, sum);
         if (idx < nch)
-            q[idx] = (uint32_t)(e0 & 0xff) | ((uint32_t)(e1 & 0xff) << 8) | ((uint32_t)(e2 & 0xff) << 16) |
-                     ((uint32_t)(e3 & 0xff) << 24);
+            q[idx] = packed;
     }
     // Zero padding up to ldq (a multiple of 4 bytes, as K is here).
     for (int64_t idx = nch + tid; idx < (ldq >> 2); idx += kThreads)
