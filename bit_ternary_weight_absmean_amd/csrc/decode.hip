@@ -346,10 +346,14 @@ __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct_db(
 // unaligned K).
 template <int MT, int S, int RX, int U>
 __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
-    const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const float *__restrict__ X, int M, int64_t N,
-    int K, int KC, int NB16, float *__restrict__ Y, int32_t *__restrict__ ACC)
+    const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const float *__restrict__ X,
+    float *__restrict__ Y, int32_t *__restrict__ ACC, int M, int N, int K)
 {
+    // The arguments fill the 13 dwords gfx950 preloads into SGPRs, so no scalar load of
+    // the kernel arguments is pending at the first barrier.
     constexpr int WAVES = kFusedWaves;
+    const int KC = (K + 63) >> 6;
+    const int NB16 = ((N + 63) >> 6) * 4;
     constexpr int T = WAVES * 64;
     // U: steps per register batch (two batches in flight), sized by the launcher to the
     // steps a wave owns, so the first two batches hold few clamped duplicate loads.
@@ -363,7 +367,6 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     const int KC4 = (KC + 3) & ~3;  // chunks in whole 256-k steps (zero-filled past KC)
     const int pitch = KC4 * 64 + kPitchPad;
 
-    const float gamma = w_scale[0];  // issued first: the epilogue needs it last
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
@@ -420,6 +423,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
         if (nb > 1)
             load_batch(wb, 1);
     }
+    // After the weights: the epilogue is the only user, and it waits for them anyway.
+    const float gamma = load_scale_vmem(w_scale);
 
     // 3. Per-token absmax: wave partials in LDS.
     float4 xr[MT][RPT];
@@ -630,12 +635,10 @@ hipError_t launch_fused_u(const uint4 *Wp, const float *w_scale, const float *X,
                           float *Y, int32_t *acc, hipStream_t s)
 {
     constexpr int RBW = kFusedWaves / S;
-    const int KC = (int)((K + 63) / 64);
-    const int NB16 = (int)(((N + 63) / 64) * 4);
     const int64_t nb16 = (N + 15) / 16;
     const dim3 grid((unsigned)((nb16 + RBW - 1) / RBW)), block(kFusedWaves * 64);
-    hipLaunchKernelGGL((k_linear_decode<MT, S, RX, U>), grid, block, fused_lds(M, K, S), s, Wp, w_scale, X, (int)M,
-                       N, (int)K, KC, NB16, Y, acc);
+    hipLaunchKernelGGL((k_linear_decode<MT, S, RX, U>), grid, block, fused_lds(M, K, S), s, Wp, w_scale, X, Y, acc,
+                       (int)M, (int)N, (int)K);
     return hipGetLastError();
 }
 

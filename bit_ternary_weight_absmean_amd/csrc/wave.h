@@ -89,6 +89,17 @@ __device__ inline uint32_t quant_pack4_sum(float4 v, float inv, int &sum)
     return lo | hi;
 }
 
+// One fp32 value every lane needs (a matrix's gamma), read as a vector-memory load. It
+// is then waited for through vmcnt, in order with the loads issued before it. A scalar
+// load is waited for through lgkmcnt, which every LDS wait and workgroup barrier before
+// the value's use also drains, so a slow read of the scale would stall those first.
+__device__ inline float load_scale_vmem(const float *p)
+{
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, 4, 0x00020000);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 0, 0, 0));
+}
+
 __device__ inline int sum_bytes_s8(uint32_t p)
 {
     return (int)(int8_t)(p & 0xff) + (int)(int8_t)((p >> 8) & 0xff) + (int)(int8_t)((p >> 16) & 0xff) +
