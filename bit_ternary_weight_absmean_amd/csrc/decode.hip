@@ -336,14 +336,28 @@ __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct_db(
 }
 
 // ------------------------------------------------------------- fused kernel
+// Bytes of one token's quantized row in LDS. The register path (RX > 0) stores every
+// slot a thread holds, RX * 512 dwords (at least the KC4 * 64 bytes the products read:
+// the launcher's RX covers K), so its stores need no per-lane guard; the streaming path
+// stores KC4 * 64 bytes. The 16-byte pad staggers the rows across LDS banks.
+__host__ __device__ constexpr int fused_pitch(int KC4, int rx)
+{
+    return (rx > 0 && rx * kFusedWaves * 64 * 4 > KC4 * 64 ? rx * kFusedWaves * 64 * 4 : KC4 * 64) + kPitchPad;
+}
+
 // Eight waves per workgroup. Wave w owns the 16-row block blockIdx.x * (8/S) + w / S
 // and the k-split w % S of it: steps st = w % S, w % S + S, ... For S = 1 a wave owns
 // all of K and its epilogue runs straight from its MFMA registers; for S > 1 the S
-// partial sums of a block are added through LDS. MT = compile-time token capacity
-// (M <= MT). RX > 0: each thread keeps RX float4 of each token in registers for the
-// quantizer (the launcher picks the smallest power of two that covers K, so the loads
-// need no guards); RX = 0: the tokens are streamed from memory twice (large or
-// unaligned K).
+// partial sums of a block are added through LDS by the block's last k-split, which owns
+// the fewest steps. MT = compile-time token capacity (M <= MT). RX > 0: each thread keeps
+// RX float4 of each token in registers for the quantizer (the launcher picks the smallest
+// power of two that covers K, so the loads need no guards); RX = 0: the tokens are
+// streamed from memory twice (large or unaligned K).
+//
+// Every instruction between the arrival of the activations and the stores is on the
+// launch's critical path (at 2B sizes the weights are in registers well before the
+// quantizer is done), and a SIMD runs two of the eight waves: the work that does not
+// need the token maxima is done before or after the two barriers around the quantizer.
 template <int MT, int S, int RX, int U>
 __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const float *__restrict__ X,
@@ -352,6 +366,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     // The arguments fill the 13 dwords gfx950 preloads into SGPRs, so no scalar load of
     // the kernel arguments is pending at the first barrier.
     constexpr int WAVES = kFusedWaves;
+    static_assert(WAVES == 8, "the token maxima are read as two float4");
     const int KC = (K + 63) >> 6;
     const int NB16 = ((N + 63) >> 6) * 4;
     constexpr int T = WAVES * 64;
@@ -359,13 +374,21 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     // steps a wave owns, so the first two batches hold few clamped duplicate loads.
     constexpr int RPT = RX > 0 ? RX : 1;
     constexpr int RBW = WAVES / S;    // row blocks per workgroup
+    constexpr bool regpath = RX > 0;  // then K4 >= 1 and K4 <= RX * T (the launcher checks)
+    // One row block per workgroup (S = 8): all eight waves' partials meet in the k-split
+    // sum, so each wave subtracts its own share of sum_k q there instead of publishing it
+    // before the second barrier.
+    constexpr bool fold_q = regpath && RBW == 1;
+    // Register path with k-splits: the wave sums of q are formed after the second barrier.
+    constexpr bool late_q = regpath && S > 1;
+    constexpr int KE = S - 1;         // the k-split that runs the epilogue
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    float *s_apart = reinterpret_cast<float *>(smem);                  // [WAVES][kMaxM]
-    int *s_qpart = reinterpret_cast<int *>(s_apart + WAVES * kMaxM);   // [WAVES][kMaxM]
+    float *s_apart = reinterpret_cast<float *>(smem);                  // [kMaxM][WAVES]
+    int *s_qpart = reinterpret_cast<int *>(s_apart + WAVES * kMaxM);   // [kMaxM][WAVES]
     int *red = s_qpart + WAVES * kMaxM;                                // [WAVES][4][64] (S > 1)
     int8_t *xq = reinterpret_cast<int8_t *>(red + (S > 1 ? WAVES * 256 : 0));
     const int KC4 = (KC + 3) & ~3;  // chunks in whole 256-k steps (zero-filled past KC)
-    const int pitch = KC4 * 64 + kPitchPad;
+    const int pitch = fused_pitch(KC4, RX);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -379,7 +402,6 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     const int nb = (nmine + U - 1) / U;
 
     const int K4 = (K + 3) >> 2;
-    constexpr bool regpath = RX > 0;  // then K4 >= 1 and K4 <= RX * T (the launcher checks)
 
     auto load4 = [&](const float *xr, int k4) -> float4 {
         if (K % 4 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0)
@@ -445,9 +467,9 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
                 for (int i = 0; i < RPT; ++i)
                     a = fmaxf(a, fmaxf(fmaxf(fabsf(xr[m][i].x), fabsf(xr[m][i].y)),
                                        fmaxf(fabsf(xr[m][i].z), fabsf(xr[m][i].w))));
-                a = wave_max_f32(a);
+                a = wave_max_nonneg_f32(a);
                 if (lane == 0)
-                    s_apart[wave * kMaxM + m] = a;
+                    s_apart[m * WAVES + wave] = a;
             }
         }
     } else {
@@ -459,26 +481,29 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
                 const float4 v = load4(xm, k4);
                 a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
             }
-            a = wave_max_f32(a);
+            a = wave_max_nonneg_f32(a);
             if (lane == 0)
-                s_apart[wave * kMaxM + m] = a;
+                s_apart[m * WAVES + wave] = a;
         }
     }
     __syncthreads();
 
-    // 4. Quantize into LDS; per-wave partial sums of q.
+    // 4. Quantize into LDS; per-lane (register path with k-splits) or per-wave partial
+    //    sums of q.
     auto token_amax = [&](int m) {
-        float amax = s_apart[m];
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w)
-            amax = fmaxf(amax, s_apart[w * kMaxM + m]);
-        return amax;
+        // the eight wave maxima, compared as bit patterns (all >= +0, none NaN)
+        const uint4 u = reinterpret_cast<const uint4 *>(s_apart + m * WAVES)[0];
+        const uint4 v = reinterpret_cast<const uint4 *>(s_apart + m * WAVES)[1];
+        const uint32_t a = max(max(max(u.x, u.y), max(u.z, u.w)), max(max(v.x, v.y), max(v.z, v.w)));
+        return __uint_as_float(a);
     };
     // absmax of the token this lane's output column holds (token r), for the epilogue.
     float amax_r = 0.0f;
+    int qlane[MT];  // late_q: this lane's sum of q per token
     if constexpr (regpath) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
+            qlane[m] = 0;
             if (m < M) {
                 const float amax = token_amax(m);
                 const float inv = (amax == 0.0f) ? 0.0f : 127.0f / amax;
@@ -488,19 +513,21 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
                 int sum = 0;
 #pragma unroll
                 for (int i = 0; i < RPT; ++i) {
-                    const int k4 = tid + i * T;
-                    if (k4 < KC4 * 16) {
-                        // xr is zero past K (masked at load): those dwords quantize to 0
+                    // Wave-uniform: skip slots wholly past the part of the row the products
+                    // read; the rest store unguarded (the pitch holds every slot, and xr is
+                    // zero past K, so the padding up to KC4 chunks comes out zero).
+                    if (wave * 64 + i * T < KC4 * 16) {
                         const uint32_t p = quant_pack4_sum(xr[m][i], inv, sum);
-                        *reinterpret_cast<uint32_t *>(qrow + lds_x_offset(k4)) = p;
+                        *reinterpret_cast<uint32_t *>(qrow + lds_x_offset(tid + i * T)) = p;
                     }
                 }
-                // zero padding past the register-held part of the row
-                for (int k4 = tid + RPT * T; k4 < KC4 * 16; k4 += T)
-                    *reinterpret_cast<uint32_t *>(qrow + lds_x_offset(k4)) = 0u;
-                sum = wave_sum_i32(sum);
-                if (lane == 0)
-                    s_qpart[wave * kMaxM + m] = sum;
+                if constexpr (late_q) {
+                    qlane[m] = sum;
+                } else {
+                    sum = wave_sum_i32(sum);
+                    if (lane == 0)
+                        s_qpart[m * WAVES + wave] = sum;
+                }
             }
         }
     } else {
@@ -518,36 +545,55 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
             }
             sum = wave_sum_i32(sum);
             if (lane == 0)
-                s_qpart[wave * kMaxM + m] = sum;
+                s_qpart[m * WAVES + wave] = sum;
         }
     }
     __syncthreads();
 
     // 5. Stream the wave's weights, two batches in flight, MFMAs on the older one.
+    //    Token columns r >= M read token M - 1 (their outputs are never stored); every
+    //    chunk read, c < 4 * nsteps <= KC4, lies in the zero-filled row.
     v4i a1[1], a4[1], a16[1];
     a1[0] = a4[0] = a16[0] = v4i{0, 0, 0, 0};
-    auto compute_batch = [&](const v4i (&w)[U], int b) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = b * U + u;
-            if (i < nmine) {
-                // c < 4 * nsteps <= KC4: inside the zero-filled row. Token columns
-                // r >= M read token M - 1 (their outputs are never stored).
-                const int c = 4 * (ks + S * i) + g;
-                const v4i *p = reinterpret_cast<const v4i *>(xq + min(r, M - 1) * pitch + c * 64);
-                const v4i b[4] = {p[0], p[1], p[2], p[3]};
-                mfma_step_t(w[u], b, a1[0], a4[0], a16[0]);
-            }
+    const int8_t *xrow = xq + min(r, M - 1) * pitch;
+    if constexpr (U == 1) {
+        // At most two steps (the launcher's batch size): both activation operands are read
+        // before the first MFMA.
+        v4i b0[4], b1[4];
+        if (nmine > 0) {
+            const v4i *p = reinterpret_cast<const v4i *>(xrow + (4 * ks + g) * 64);
+            b0[0] = p[0], b0[1] = p[1], b0[2] = p[2], b0[3] = p[3];
         }
-    };
-    for (int b = 0; b < nb; b += 2) {
-        compute_batch(wa, b);
-        if (b + 2 < nb)
-            load_batch(wa, b + 2);
-        if (b + 1 < nb) {
-            compute_batch(wb, b + 1);
-            if (b + 3 < nb)
-                load_batch(wb, b + 3);
+        if (nmine > 1) {
+            const v4i *p = reinterpret_cast<const v4i *>(xrow + (4 * (ks + S) + g) * 64);
+            b1[0] = p[0], b1[1] = p[1], b1[2] = p[2], b1[3] = p[3];
+        }
+        if (nmine > 0)
+            mfma_step_t(wa[0], b0, a1[0], a4[0], a16[0]);
+        if (nmine > 1)
+            mfma_step_t(wb[0], b1, a1[0], a4[0], a16[0]);
+    } else {
+        auto compute_batch = [&](const v4i (&w)[U], int b) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = b * U + u;
+                if (i < nmine) {
+                    const int c = 4 * (ks + S * i) + g;
+                    const v4i *p = reinterpret_cast<const v4i *>(xrow + c * 64);
+                    const v4i b[4] = {p[0], p[1], p[2], p[3]};
+                    mfma_step_t(w[u], b, a1[0], a4[0], a16[0]);
+                }
+            }
+        };
+        for (int b = 0; b < nb; b += 2) {
+            compute_batch(wa, b);
+            if (b + 2 < nb)
+                load_batch(wa, b + 2);
+            if (b + 1 < nb) {
+                compute_batch(wb, b + 1);
+                if (b + 3 < nb)
+                    load_batch(wb, b + 3);
+            }
         }
     }
 
@@ -557,38 +603,76 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
 #pragma unroll
     for (int v = 0; v < 4; ++v)
         part[v] = a1[0][v] + (a4[0][v] >> 2) + (a16[0][v] >> 4);
-    if (S > 1) {
+    if constexpr (late_q) {
+        int qr = 0;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            red[(wave * 4 + v) * 64 + lane] = part[v];
+        for (int m = 0; m < MT; ++m) {
+            if (m < M) {
+                const int qw = wave_sum_i32(qlane[m]);
+                if constexpr (fold_q) {
+                    if (m == r)
+                        qr = qw;
+                } else if (lane == 0) {
+                    s_qpart[m * WAVES + wave] = qw;
+                }
+            }
+        }
+        if constexpr (fold_q) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                part[v] -= qr;
+        }
+    }
+    // The epilogue wave's scale, formed before it waits for the other k-splits (it owns
+    // the fewest steps, so it reaches the barrier first).
+    float scale = 0.0f;
+    if (ks == KE)
+        scale = gamma * ((amax_r == 0.0f) ? 0.0f : amax_r / 127.0f);
+    if constexpr (S > 1) {
+        if (ks != KE) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                red[(wave * 4 + v) * 64 + lane] = part[v];
+        }
         __syncthreads();
-        if (ks == 0) {
+        if (ks == KE) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 int sum = part[v];
 #pragma unroll
-                for (int j = 1; j < S; ++j)
-                    sum += red[((wave + j) * 4 + v) * 64 + lane];
+                for (int j = 0; j < KE; ++j)
+                    sum += red[((wave - KE + j) * 4 + v) * 64 + lane];
                 part[v] = sum;
             }
         }
     }
-    if (ks == 0 && r < M) {
-        int qs = s_qpart[r];
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w)
-            qs += s_qpart[w * kMaxM + r];
-        const float scale = gamma * ((amax_r == 0.0f) ? 0.0f : amax_r / 127.0f);
+    if (ks == KE && r < M) {
+        int qs = 0;
+        if constexpr (!fold_q) {
+            const int4 u = reinterpret_cast<const int4 *>(s_qpart + r * WAVES)[0];
+            const int4 v = reinterpret_cast<const int4 *>(s_qpart + r * WAVES)[1];
+            qs = (u.x + u.y) + (u.z + u.w) + (v.x + v.y) + (v.z + v.w);
+        }
         const int64_t n0 = (int64_t)b16 * 16 + 4 * g;
+        if ((N & 3) == 0 && n0 < N && ((reinterpret_cast<uintptr_t>(Y) | reinterpret_cast<uintptr_t>(ACC)) & 15) == 0) {
+            // four consecutive outputs of one row of y (N % 4 == 0 keeps the row 16-byte aligned)
+            const int4 acc = make_int4(part[0] - qs, part[1] - qs, part[2] - qs, part[3] - qs);
+            if (ACC)
+                *reinterpret_cast<int4 *>(ACC + (int64_t)r * N + n0) = acc;
+            if (Y)
+                *reinterpret_cast<float4 *>(Y + (int64_t)r * N + n0) =
+                    make_float4((float)acc.x * scale, (float)acc.y * scale, (float)acc.z * scale, (float)acc.w * scale);
+        } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t n = n0 + v;
-            if (n < N) {
-                const int acc = part[v] - qs;
-                if (ACC)
-                    ACC[(int64_t)r * N + n] = acc;
-                if (Y)
-                    Y[(int64_t)r * N + n] = (float)acc * scale;
+            for (int v = 0; v < 4; ++v) {
+                const int64_t n = n0 + v;
+                if (n < N) {
+                    const int acc = part[v] - qs;
+                    if (ACC)
+                        ACC[(int64_t)r * N + n] = acc;
+                    if (Y)
+                        Y[(int64_t)r * N + n] = (float)acc * scale;
+                }
             }
         }
     }
@@ -623,11 +707,24 @@ int pick_s(int64_t N)
     return s;
 }
 
-size_t fused_lds(int64_t M, int64_t K, int s)
+size_t fused_lds(int64_t M, int64_t K, int s, int rx)
 {
     const int64_t KC = (K + 63) / 64;
-    const int64_t KC4 = (KC + 3) / 4 * 4;
-    return 2 * kFusedWaves * kMaxM * 4 + (s > 1 ? kFusedWaves * 256 * 4 : 0) + (size_t)M * (KC4 * 64 + kPitchPad);
+    const int KC4 = (int)((KC + 3) / 4 * 4);
+    return 2 * kFusedWaves * kMaxM * 4 + (s > 1 ? kFusedWaves * 256 * 4 : 0) + (size_t)M * fused_pitch(KC4, rx);
+}
+
+// The register path's float4 per thread and token (0: streaming path), as launch_fused_t
+// picks it for 16-byte aligned activations; it sets the LDS row pitch.
+int fused_rx(int64_t M, int64_t K)
+{
+    const int64_t K4 = K / 4, T = kFusedWaves * 64;
+    if (K <= 0 || (K & 3) != 0)
+        return 0;
+    int rx = 1;
+    while ((int64_t)rx * T < K4)
+        rx *= 2;
+    return rx * pick_mt(M) > kXRegs ? 0 : rx;
 }
 
 template <int MT, int S, int RX, int U>
@@ -637,7 +734,7 @@ hipError_t launch_fused_u(const uint4 *Wp, const float *w_scale, const float *X,
     constexpr int RBW = kFusedWaves / S;
     const int64_t nb16 = (N + 15) / 16;
     const dim3 grid((unsigned)((nb16 + RBW - 1) / RBW)), block(kFusedWaves * 64);
-    hipLaunchKernelGGL((k_linear_decode<MT, S, RX, U>), grid, block, fused_lds(M, K, S), s, Wp, w_scale, X, Y, acc,
+    hipLaunchKernelGGL((k_linear_decode<MT, S, RX, U>), grid, block, fused_lds(M, K, S, RX), s, Wp, w_scale, X, Y, acc,
                        (int)M, (int)N, (int)K);
     return hipGetLastError();
 }
@@ -717,7 +814,8 @@ hipError_t launch_direct_t(const uint4 *Wp, const float *w_scale, const int8_t *
 
 }  // namespace
 
-size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K) { return fused_lds(M, K, pick_s(N)); }
+// An upper bound for any activation alignment: the register path's pitch is the larger.
+size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K) { return fused_lds(M, K, pick_s(N), fused_rx(M, K)); }
 
 hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq,
                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,

@@ -8,10 +8,13 @@
 
 namespace bt {
 
+// Every control used below reads a lane of the same 16-lane row, so no lane is masked
+// and the fill value never shows; passing 0 with bound_ctrl lets the compiler fold the
+// move into the instruction that consumes it (that instruction's DPP form).
 template <int CTRL>
 __device__ inline int dpp_i(int v)
 {
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
 }
 
 constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
@@ -35,11 +38,12 @@ __device__ inline uint32_t wave_reduce_bits(uint32_t v, Op op)
     return v;
 }
 
-__device__ inline float wave_max_f32(float v)
+// Maximum of values that are >= +0 and not NaN (absolute values reduced with fmaxf from
+// 0): their bit patterns order like the values, so an unsigned maximum gives the same
+// result without the float maximum's canonicalization of each operand.
+__device__ inline float wave_max_nonneg_f32(float v)
 {
-    return __uint_as_float(wave_reduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
-        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
-    }));
+    return __uint_as_float(wave_reduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) { return a > b ? a : b; }));
 }
 
 __device__ inline int wave_sum_i32(int v)

@@ -436,7 +436,10 @@ def test_side_stream_and_graph_replay():
 # Shapes the fused kernel takes (M <= 4 and M * K <= 32768), token counts 1, 2 and 4
 # (the kernel's three token capacities), ragged and aligned K.
 LINEAR_CASES = [(1, 1, 1), (1, 100, 300), (2, 130, 129), (3, 65, 1000), (4, 200, 700), (4, 64, 64),
-                (4, 300, 517), (4, 1000, 2560), (1, 2560, 6912), (1, 600, 28672), (4, 4096, 8192)]
+                (4, 300, 517), (4, 1000, 2560), (1, 2560, 6912), (1, 600, 28672), (4, 4096, 8192),
+                # several tokens with fewer k-splits: S = 2 (four row blocks per workgroup),
+                # S = 1 (eight), S = 4 (two)
+                (4, 9000, 1000), (2, 20000, 520), (3, 8192, 1000)]
 
 
 @pytest.mark.parametrize("M,N,K", LINEAR_CASES)
