@@ -397,10 +397,6 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     const int r = lane & 15;
     const int ks = wave % S;
     const int b16 = blockIdx.x * RBW + wave / S;
-    const int nsteps = (KC + 3) >> 2;
-    const int nmine = (ks < nsteps) ? (nsteps - 1 - ks) / S + 1 : 0;
-    const int nb = (nmine + U - 1) / U;
-
     const int K4 = (K + 3) >> 2;
 
     auto load4 = [&](const float *xr, int k4) -> float4 {
@@ -421,11 +417,15 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
         for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int i = 0; i < RPT; ++i)
-                xraw[m][i] = X4[(int64_t)min(m, M - 1) * K4 + min(tid + i * T, K4 - 1)];
+                xraw[m][i] = X4[(m == 0 ? 0 : (int64_t)min(m, M - 1) * K4) + min(tid + i * T, K4 - 1)];
         // Keep them ahead of the weight loads in issue order: the quantizer then waits
-        // for the activations only (vector-memory operations complete in order).
+        // for the activations only (vector-memory operations complete in order). Nothing
+        // else is computed before them.
         __builtin_amdgcn_sched_barrier(0);
     }
+    const int nsteps = (KC + 3) >> 2;
+    const int nmine = (ks < nsteps) ? (nsteps - 1 - ks) / S + 1 : 0;
+    const int nb = (nmine + U - 1) / U;
 
     // 2. The wave's first weight batch.
     v4i wa[U], wb[U];
@@ -750,6 +750,8 @@ hipError_t launch_fused_rx(const uint4 *Wp, const float *w_scale, const float *X
         return launch_fused_u<MT, S, RX, 1>(Wp, w_scale, X, M, N, K, Y, acc, s);
     if (mine <= 4)
         return launch_fused_u<MT, S, RX, 2>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    if (mine <= 6)
+        return launch_fused_u<MT, S, RX, 3>(Wp, w_scale, X, M, N, K, Y, acc, s);
     return launch_fused_u<MT, S, RX, 4>(Wp, w_scale, X, M, N, K, Y, acc, s);
 }
 
