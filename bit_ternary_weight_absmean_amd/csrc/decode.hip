@@ -385,8 +385,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float *s_apart = reinterpret_cast<float *>(smem);                  // [kMaxM][WAVES]
     int *s_qpart = reinterpret_cast<int *>(s_apart + WAVES * kMaxM);   // [kMaxM][WAVES]
-    int *red = s_qpart + WAVES * kMaxM;                                // [WAVES][4][64] (S > 1)
-    int8_t *xq = reinterpret_cast<int8_t *>(red + (S > 1 ? WAVES * 256 : 0));
+    int4 *red = reinterpret_cast<int4 *>(s_qpart + WAVES * kMaxM);    // [WAVES][64] (S > 1)
+    int8_t *xq = reinterpret_cast<int8_t *>(red + (S > 1 ? WAVES * 64 : 0));
     const int KC4 = (KC + 3) & ~3;  // chunks in whole 256-k steps (zero-filled past KC)
     const int pitch = fused_pitch(KC4, RX);
 
@@ -629,20 +629,14 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     if (ks == KE)
         scale = gamma * ((amax_r == 0.0f) ? 0.0f : amax_r / 127.0f);
     if constexpr (S > 1) {
-        if (ks != KE) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                red[(wave * 4 + v) * 64 + lane] = part[v];
-        }
+        if (ks != KE)
+            red[wave * 64 + lane] = make_int4(part[0], part[1], part[2], part[3]);
         __syncthreads();
         if (ks == KE) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                int sum = part[v];
-#pragma unroll
-                for (int j = 0; j < KE; ++j)
-                    sum += red[((wave - KE + j) * 4 + v) * 64 + lane];
-                part[v] = sum;
+            for (int j = 0; j < KE; ++j) {
+                const int4 o = red[(wave - KE + j) * 64 + lane];
+                part[0] += o.x, part[1] += o.y, part[2] += o.z, part[3] += o.w;
             }
         }
     }
