@@ -44,8 +44,12 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_quant_act.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.oracle_ternary_matmul.argtypes = [vp, vp, i64, i64, i64, vp]
     lib.oracle_scale_epilogue.argtypes = [vp, ctypes.c_float, vp, i64, i64, vp]
+    lib.oracle_absmean_rows.argtypes = [vp, i64, i64, vp, i64, vp]
+    lib.oracle_ternarize_rows.argtypes = [vp, i64, i64, vp, vp]
+    lib.oracle_scale_epilogue_rows.argtypes = [vp, vp, vp, i64, i64, vp]
     for f in ("oracle_absmean", "oracle_ternarize", "oracle_quant_act",
-              "oracle_ternary_matmul", "oracle_scale_epilogue"):
+              "oracle_ternary_matmul", "oracle_scale_epilogue", "oracle_absmean_rows",
+              "oracle_ternarize_rows", "oracle_scale_epilogue_rows"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -71,6 +75,8 @@ def _f32(a) -> np.ndarray:
 
 
 def _check(rc: int) -> None:
+    if rc == 2:
+        raise OracleInputError("the row groups do not cover the rows exactly")
     if rc != 0:
         raise OracleInputError("oracle rejected a non-finite input")
 
@@ -158,3 +164,58 @@ def linear(W, X, lib=None) -> dict:
     acc = ternary_matmul(T, Q, lib)
     Y = scale_epilogue(acc, gamma, s_x, lib)
     return {"gamma": gamma, "T": T, "Q": Q, "s_x": s_x, "qsum": qsum, "acc": acc, "Y": Y}
+
+
+def absmean_rows(W, seg_rows=None, lib=None) -> np.ndarray:
+    """Row-group scales: row_scale[n] = mean|W| over row n's group (fp32 [N]).
+
+    ``seg_rows`` lists the group sizes in row order (None: one group per row).
+    BitNet GPU guide, "Frequently Asked Questions" (model-specific scales and group
+    dimensions).
+    """
+    lib = lib or load()
+    W = _f32(W)
+    N, K = W.shape
+    out = np.empty(N, dtype=np.float32)
+    if seg_rows is None:
+        _check(lib.oracle_absmean_rows(_ptr(W), N, K, None, 0, _ptr(out)))
+    else:
+        seg = np.ascontiguousarray(seg_rows, dtype=np.int64)
+        _check(lib.oracle_absmean_rows(_ptr(W), N, K, _ptr(seg), len(seg), _ptr(out)))
+    return out
+
+
+def ternarize_rows(W, row_scale, lib=None) -> np.ndarray:
+    """Codes of each row against its own scale (the exact compare of ``ternarize``)."""
+    lib = lib or load()
+    W = _f32(W)
+    N, K = W.shape
+    rs = _f32(row_scale)
+    T = np.empty((N, K), dtype=np.int8)
+    _check(lib.oracle_ternarize_rows(_ptr(W), N, K, _ptr(rs), _ptr(T)))
+    return T
+
+
+def scale_epilogue_rows(acc, row_scale, s_x, lib=None) -> np.ndarray:
+    """y = acc * gamma_n * s_x[m] in fp64, rounded once to fp32.
+
+    "bit-floor" page, "The core math", with the weight scale of output row n.
+    """
+    lib = lib or load()
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    rs, s_x = _f32(row_scale), _f32(s_x)
+    M, N = acc.shape
+    Y = np.empty((M, N), dtype=np.float32)
+    _check(lib.oracle_scale_epilogue_rows(_ptr(acc), _ptr(rs), _ptr(s_x), M, N, _ptr(Y)))
+    return Y
+
+
+def linear_rows(W, X, seg_rows=None, lib=None) -> dict:
+    """The linear layer with row-group weight scales: every intermediate, as a dict."""
+    lib = lib or load()
+    row_scale = absmean_rows(W, seg_rows, lib)
+    T = ternarize_rows(W, row_scale, lib)
+    Q, s_x, qsum = quant_act(X, lib)
+    acc = ternary_matmul(T, Q, lib)
+    Y = scale_epilogue_rows(acc, row_scale, s_x, lib)
+    return {"row_scale": row_scale, "T": T, "Q": Q, "s_x": s_x, "qsum": qsum, "acc": acc, "Y": Y}

@@ -34,9 +34,15 @@
  *      rounded), q = clamp(rint(x * inv), -127, 127) with rint half-to-even,
  *      s_x = a / 127.0f; a zero row gives q = 0 and s_x = 0;
  *  R5  y = acc * gamma * s_x evaluated in fp64 and rounded once to fp32;
- *  R6  non-finite inputs are outside the contract: the oracle rejects them.
+ *  R6  non-finite inputs are outside the contract: the oracle rejects them;
+ *  R7  row-group scales (the "_rows" functions): the rows of W are cut, in order,
+ *      into groups that are separate matrices stored one above the other (the Q,
+ *      K and V blocks of a fused projection; one row per group at the finest);
+ *      each group gets the R2 scale of its own rows, its codes use that scale
+ *      (R3), and y uses the scale of its output row (R5 with gamma_n).
  *
- * Every entry point returns 0 on success and 1 when an input is not finite.
+ * Every entry point returns 0 on success and 1 when an input is not finite
+ * (2 when the row groups do not cover the N rows exactly).
  */
 #include <math.h>
 #include <stdint.h>
@@ -157,5 +163,51 @@ int oracle_scale_epilogue(const int32_t *acc, float gamma, const float *s_x,
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
             Y[m * N + n] = (float)((double)acc[m * N + n] * (double)gamma * (double)s_x[m]);
+    return 0;
+}
+
+/* Row-group weight scales (R7): the rows are cut, in order, into nseg groups of
+ * seg_rows[s] >= 1 rows (seg_rows == NULL: each of the N rows is its own group);
+ * row_scale[n] receives the mean |W| of row n's group alone, summed as in R2.
+ * Follows the BitNet GPU guide, "Frequently Asked Questions" (the kernel wrapper
+ * assumes model-specific quantization scales and group dimensions). */
+int oracle_absmean_rows(const float *W, int64_t N, int64_t K, const int64_t *seg_rows,
+                        int64_t nseg, float *row_scale)
+{
+    const int64_t groups = seg_rows ? nseg : N;
+    int64_t n0 = 0;
+    for (int64_t s = 0; s < groups; ++s) {
+        const int64_t rows = seg_rows ? seg_rows[s] : 1;
+        if (rows < 1 || n0 + rows > N)
+            return 2;
+        float g;
+        if (oracle_absmean(W + n0 * K, rows, K, &g))
+            return 1;
+        for (int64_t n = n0; n < n0 + rows; ++n)
+            row_scale[n] = g;
+        n0 += rows;
+    }
+    return n0 == N ? 0 : 2;
+}
+
+/* Codes of every row against its own scale (R3 with gamma_n, R7). */
+int oracle_ternarize_rows(const float *W, int64_t N, int64_t K, const float *row_scale,
+                          int8_t *T)
+{
+    for (int64_t n = 0; n < N; ++n)
+        if (oracle_ternarize(W + n * K, 1, K, row_scale[n], T + n * K))
+            return 1;
+    return 0;
+}
+
+/* y[m,n] = acc[m,n] * gamma_n * s_x[m], in fp64, rounded once to fp32 (R5, R7).
+ * Follows the "bit-floor" page, "The core math" (weight scale times activation
+ * scale times the integer dot), with the weight scale of output row n. */
+int oracle_scale_epilogue_rows(const int32_t *acc, const float *row_scale, const float *s_x,
+                               int64_t M, int64_t N, float *Y)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            Y[m * N + n] = (float)((double)acc[m * N + n] * (double)row_scale[n] * (double)s_x[m]);
     return 0;
 }

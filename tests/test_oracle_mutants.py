@@ -24,12 +24,18 @@ MUTANTS = {
                              "for (int64_t k = 0; k < K - 1; ++k) {\n            float w = W[n * K + k];"),
     "mean_without_abs": ("row += fabs((double)w);", "row += (double)w;"),
     "transposed_weight_index": ("(int32_t)T[n * K + k]", "(int32_t)T[k * N + n]"),
-    "epilogue_drops_sx": (" * (double)s_x[m]);", ");"),
+    "epilogue_drops_sx": ("(double)gamma * (double)s_x[m]);", "(double)gamma);"),
     "epilogue_drops_gamma": ("(double)acc[m * N + n] * (double)gamma", "(double)acc[m * N + n]"),
     "negative_code_sign": ("T[i] = -1;", "T[i] = 1;"),
     "int8_scale_128": ("const float inv = 127.0f / a;", "const float inv = 128.0f / a;"),
     "sx_inverted": ("s_x[m] = a / 127.0f;", "s_x[m] = 127.0f / a;"),
     "qsum_dropped": ("sum += (int32_t)r;", "(void)r;"),
+    "rows_epilogue_token_index": ("(double)row_scale[n] * (double)s_x[m]", "(double)row_scale[m] * (double)s_x[m]"),
+    "rows_group_from_first_row": ("if (oracle_absmean(W + n0 * K, rows, K, &g))",
+                                  "if (oracle_absmean(W + n0 * K, 1, K, &g))"),
+    "rows_codes_first_scale": ("row_scale[n], T + n * K", "row_scale[0], T + n * K"),
+    "rows_group_start_stuck": ("        n0 += rows;\n    }\n    return n0 == N", "        n0 += 0;\n    }\n    return n0 == N"),
+    "rows_epilogue_drops_scale": ("(double)acc[m * N + n] * (double)row_scale[n]", "(double)acc[m * N + n]"),
 }
 
 
@@ -49,7 +55,9 @@ def _battery(lib):
                  "test_add_subtract_skip_form", "test_gamma_is_exact_mean_rounded", "test_zero_fraction_gaussian",
                  "test_quant_rounding_bound_and_range", "test_quant_odd_and_scale_invariant",
                  "test_negating_w_negates_y", "test_y_equals_matmul_of_dequantized_operands",
-                 "test_bitplane_popcount_form"):
+                 "test_bitplane_popcount_form", "test_row_group_scales_are_exact_group_means",
+                 "test_row_group_codes_gaussian_zero_fraction", "test_row_scales_power_of_two_rows",
+                 "test_one_group_is_the_per_matrix_layer", "test_row_groups_equal_separate_matrices"):
         run(name, getattr(pins, name))
     return failed
 

@@ -341,3 +341,99 @@ def test_nonfinite_rejected(orc):
     X[0, 0] = np.inf
     with pytest.raises(oracle.OracleInputError):
         oracle.quant_act(X, orc)
+
+
+# ----------------------------------------------------- row-group weight scales
+_GROUPS = [640, 128, 128]  # a fused projection: one large block, then two small ones
+
+
+def _grouped_weights(seed, scales=(1.0, 30.0, 0.05)):
+    """Three row groups of very different magnitudes, so that a scale taken over the
+    wrong rows changes the codes of a whole group."""
+    W = synth.gaussian((sum(_GROUPS), 96), seed, 0.02)
+    out, n0 = W.copy(), 0
+    for rows, c in zip(_GROUPS, scales):
+        out[n0:n0 + rows] *= np.float32(c)
+        n0 += rows
+    return out
+
+
+def test_row_group_scales_are_exact_group_means(orc):
+    """Every row's scale is fp32(exact mean |W| over its own group) (math.fsum is exact),
+    for explicit groups and for one group per row."""
+    W = _grouped_weights(400)
+    rs = oracle.absmean_rows(W, _GROUPS, orc)
+    n0 = 0
+    for rows in _GROUPS:
+        blk = W[n0:n0 + rows]
+        exact = np.float32(math.fsum(np.abs(blk.astype(np.float64)).ravel().tolist()) / blk.size)
+        assert np.all(np.abs(rs[n0:n0 + rows].astype(np.float64) - float(exact)) <= np.spacing(exact)), n0
+        n0 += rows
+    rr = oracle.absmean_rows(W[:50], None, orc)
+    for n in range(50):
+        exact = np.float32(math.fsum(np.abs(W[n].astype(np.float64)).tolist()) / W.shape[1])
+        assert abs(float(rr[n]) - float(exact)) <= np.spacing(exact), n
+
+
+def test_row_group_codes_gaussian_zero_fraction(orc):
+    """With each group's own scale, every group of a N(0, s_g^2) matrix has the Gaussian
+    zero fraction 0.3101 whatever s_g; one scale over all rows would zero almost all of
+    the small group and almost none of the large one."""
+    W = _grouped_weights(410)
+    rs = oracle.absmean_rows(W, _GROUPS, orc)
+    T = oracle.ternarize_rows(W, rs, orc)
+    p0 = math.erf(math.sqrt(2 / math.pi) / 2 / math.sqrt(2))
+    n0 = 0
+    for rows in _GROUPS:
+        frac0 = float(np.mean(T[n0:n0 + rows] == 0))
+        # 128 x 96 draws: standard error ~0.004; 5 sigma
+        assert abs(frac0 - p0) < 0.02, (n0, frac0)
+        n0 += rows
+
+
+def test_row_scales_power_of_two_rows(orc):
+    """Scaling row n of W by 2^e_n leaves the codes and acc unchanged and scales that
+    row's scale and every y[:, n] by exactly 2^e_n (one group per row)."""
+    W = synth.gaussian((48, 200), 420, 0.02)
+    X = synth.gaussian((5, 200), 421)
+    e = np.random.default_rng(3).integers(-6, 7, size=48)
+    W2 = W * np.exp2(e).astype(np.float32)[:, None]
+    r = oracle.linear_rows(W, X, None, orc)
+    r2 = oracle.linear_rows(W2, X, None, orc)
+    np.testing.assert_array_equal(r2["T"], r["T"])
+    np.testing.assert_array_equal(r2["acc"], r["acc"])
+    np.testing.assert_array_equal(r2["row_scale"], r["row_scale"] * np.exp2(e).astype(np.float32))
+    np.testing.assert_array_equal(r2["Y"], r["Y"] * np.exp2(e).astype(np.float32)[None, :])
+
+
+def test_one_group_is_the_per_matrix_layer(orc):
+    """A single group reduces every step to the per-matrix layer."""
+    W = synth.gaussian((70, 130), 430, 0.02)
+    X = synth.gaussian((3, 130), 431)
+    r = oracle.linear(W, X, orc)
+    rr = oracle.linear_rows(W, X, [70], orc)
+    assert np.all(rr["row_scale"] == r["gamma"])
+    for key in ("T", "acc", "Y"):
+        np.testing.assert_array_equal(rr[key], r[key])
+
+
+def test_row_groups_equal_separate_matrices(orc):
+    """A stacked matrix with per-group scales gives, block by block, what each block gives
+    as a matrix of its own (acc and y of the same activations)."""
+    W = _grouped_weights(440)
+    X = synth.gaussian((4, 96), 441)
+    rr = oracle.linear_rows(W, X, _GROUPS, orc)
+    n0 = 0
+    for rows in _GROUPS:
+        r = oracle.linear(W[n0:n0 + rows], X, orc)
+        np.testing.assert_array_equal(rr["T"][n0:n0 + rows], r["T"])
+        np.testing.assert_array_equal(rr["acc"][:, n0:n0 + rows], r["acc"])
+        np.testing.assert_array_equal(rr["Y"][:, n0:n0 + rows], r["Y"])
+        n0 += rows
+
+
+def test_row_groups_must_cover_the_rows(orc):
+    W = synth.gaussian((10, 8), 450, 0.02)
+    for bad in ([4, 5], [4, 7], [0, 10], [10, 0]):
+        with pytest.raises(oracle.OracleInputError):
+            oracle.absmean_rows(W, bad, orc)
