@@ -1,6 +1,6 @@
 """Benchmark of the W1.58A8 ternary linear layer hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--m M] [--split] [--eager]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--m M] [--split] [--row-scales] [--eager]
                     [--no-cpu-baseline]
 
 A step is one pass of the whole per-call hot path over one batch of synthetic input:
@@ -9,7 +9,9 @@ the integer ternary product and apply the scale epilogue -- one bt_ternary_linea
 per matrix (a single fused kernel at decode sizes; bt_quant_act + bt_ternary_gemm_ws for
 prefill, which splits K over several workgroups per tile where the tiles alone would
 leave the GPU idle). ``--split`` times the same two launches called one by one
-(bt_quant_act + bt_ternary_gemv / bt_ternary_gemm_ws) instead. Weight packing is offline and outside the timed region. Inputs
+(bt_quant_act + bt_ternary_gemv / bt_ternary_gemm_ws) instead. ``--row-scales`` packs the
+fused Q/K/V and gate/up matrices with one weight scale per block (bt_pack_weights_rows)
+and runs the row-scale entry points. Weight packing is offline and outside the timed region. Inputs
 are resident in HBM before timing starts; the step is replayed as one HIP graph.
 Prints ONE JSON line.
 
@@ -65,6 +67,9 @@ def parse():
     p.add_argument("--m", type=int, default=None, help="tokens per call (default: 1 for decode, 2048 for prefill)")
     p.add_argument("--eager", action="store_true", help="launch kernels one by one instead of replaying graphs")
     p.add_argument("--split", action="store_true", help="time bt_quant_act + product as two launches per matrix")
+    p.add_argument("--row-scales", action="store_true",
+                   help="row-group weight scales: fused Q/K/V and gate/up matrices packed with one scale per "
+                        "block (bt_pack_weights_rows), products through the row-scale entry points")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     p.add_argument("--calib-copy", action="store_true",
@@ -97,16 +102,24 @@ def workload_spec(name, m):
                 desc="2B-class prefill GEMMs, 30 layers resident")
 
 
+# Weight-scale bytes per call: one fp32 gamma, or N row scales with --row-scales.
+ROW_SCALES = False
+
+
+def scale_bytes(N):
+    return 4 * N if ROW_SCALES else 4
+
+
 def gemv_bytes(M, N, K):
     """Algorithmic HBM bytes of one product call on pre-quantized activations: 2-bit
-    weights, int8 activations read, fp32 output written, gamma + s_x + sum q read."""
-    return N * K // 4 + M * K + 4 * M * N + 4 + 8 * M
+    weights, int8 activations read, fp32 output written, weight scale(s) + s_x + sum q read."""
+    return N * K // 4 + M * K + 4 * M * N + scale_bytes(N) + 8 * M
 
 
 def linear_bytes(M, N, K):
     """Algorithmic HBM bytes of one fused call: 2-bit weights and fp32 activations read,
-    fp32 output written, gamma read."""
-    return N * K // 4 + 4 * M * K + 4 * M * N + 4
+    fp32 output written, weight scale(s) read."""
+    return N * K // 4 + 4 * M * K + 4 * M * N + scale_bytes(N)
 
 
 def quant_bytes(M, K):
@@ -146,9 +159,12 @@ def run_gpu(args, spec):
     t0 = time.time()
     for layer in range(spec["layers"]):
         row = []
-        for j, (_, N, K) in enumerate(shapes):
+        for j, (name, N, K) in enumerate(shapes):
             W = synth.device_gaussian((N, K), synth.weight_seed(cfg, layer, j), dev, std=synth.WEIGHT_STD)
-            row.append(bt.pack_weights(W, workspace=ws))
+            if ROW_SCALES:
+                row.append(bt.pack_weights_rows(W, synth.row_groups(cfg, name, N), workspace=ws))
+            else:
+                row.append(bt.pack_weights(W, workspace=ws))
             del W
         packed.append(row)
     torch.cuda.synchronize()
@@ -412,6 +428,8 @@ def summarize_mfma(args):
 
 def mfma_util_for(spec, kernel):
     """Mean MfmaUtil (%) from the committed counter summary, while the kernel sources still match."""
+    if ROW_SCALES:
+        return None  # the committed counters were taken with one scale per matrix
     path = os.path.join(ROOT, "profiles", f"mfma_{kernel}_{spec['name']}_m{spec['M']}.json")
     if not os.path.exists(path):
         return None
@@ -423,6 +441,8 @@ def mfma_util_for(spec, kernel):
 
 
 def traffic_for(spec, kernel):
+    if ROW_SCALES:
+        return None  # the committed counters were taken with one scale per matrix
     path = traffic_path(spec["name"], kernel, spec["M"])
     if not os.path.exists(path):
         return None
@@ -450,7 +470,11 @@ def main():
     if args.calib_copy:
         calib_copy()
         return 0
+    global ROW_SCALES
+    ROW_SCALES = args.row_scales
     spec = workload_spec(args.workload, args.m)
+    if ROW_SCALES:
+        spec["desc"] += ", row-group weight scales (one per Q, K, V and gate, up block)"
     g = run_gpu(args, spec)
     M = spec["M"]
     prod_us = g["ms_prod"] * 1e3 / g["n_prod"]

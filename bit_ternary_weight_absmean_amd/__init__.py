@@ -4,7 +4,8 @@ The compute lives in ``libbt.so`` (hand-written HIP kernels for gfx950 behind th
 of ``include/bt.h``). This module only marshals torch tensors (device memory) and the
 current HIP stream into those calls; every step of the path runs in the library's
 kernels. Names follow the C ABI: ``pack_weights``, ``quant_act``, ``ternary_gemv``,
-``ternary_gemm`` (+ ``unpack_weights``, ``linear``).
+``ternary_gemm`` (+ ``unpack_weights``, ``linear``, and ``pack_weights_rows`` for
+row-group weight scales, which the product calls then take in place of one scale).
 """
 from __future__ import annotations
 
@@ -21,6 +22,7 @@ from .api import (
     linear,
     linear_workspace_bytes,
     pack_weights,
+    pack_weights_rows,
     pack_workspace_bytes,
     packed_weight_bytes,
     quant_act,
@@ -31,6 +33,6 @@ from .api import (
 
 __all__ = [
     "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_MFMA", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
-    "gemm_workspace", "gemm_workspace_bytes", "linear", "linear_workspace_bytes", "pack_weights", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
+    "gemm_workspace", "gemm_workspace_bytes", "linear", "linear_workspace_bytes", "pack_weights", "pack_weights_rows", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
     "ternary_gemv", "unpack_weights",
 ]

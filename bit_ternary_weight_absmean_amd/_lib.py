@@ -24,6 +24,10 @@ SIGNATURES = {
     "bt_ternary_gemm_ws": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
     "bt_linear_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bt_ternary_linear": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "bt_pack_weights_rows": (_i32, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp]),
+    "bt_ternary_gemv_rs": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _i32, _vp]),
+    "bt_ternary_gemm_rs": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "bt_ternary_linear_rs": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "bt_status_str": (ctypes.c_char_p, [_i32]),
     "bt_last_error": (ctypes.c_char_p, []),
 }

@@ -6,6 +6,7 @@ returned status. Nothing here computes any part of the method.
 """
 from __future__ import annotations
 
+import ctypes
 from dataclasses import dataclass
 
 import torch
@@ -47,12 +48,13 @@ def pack_workspace_bytes(N: int, K: int) -> int:
 
 @dataclass
 class PackedWeight:
-    """A 2-bit packed ternary weight matrix and its absmean scale (both on device)."""
+    """A 2-bit packed ternary weight matrix and its absmean scale(s) (both on device)."""
 
     data: torch.Tensor   # uint8 [packed_weight_bytes(N, K)]
-    scale: torch.Tensor  # float32 [1], gamma
+    scale: torch.Tensor  # float32 [1] gamma, or [N] row scales when row_scales
     N: int
     K: int
+    row_scales: bool = False
 
 
 def pack_weights(W: torch.Tensor, workspace: torch.Tensor | None = None) -> PackedWeight:
@@ -69,6 +71,29 @@ def pack_weights(W: torch.Tensor, workspace: torch.Tensor | None = None) -> Pack
         raise ValueError("workspace too small")
     check(lib().bt_pack_weights(_ptr(W), N, K, _ptr(data), _ptr(scale), _ptr(workspace), _stream(dev)))
     return PackedWeight(data, scale, N, K)
+
+
+def pack_weights_rows(W: torch.Tensor, group_rows=None, workspace: torch.Tensor | None = None) -> PackedWeight:
+    """bt_pack_weights_rows: packing with row-group scales (``group_rows``: the rows of each
+    group in order, summing to N; None: one group per row). The result carries N row scales."""
+    _need(W, "W", torch.float32)
+    N, K = W.shape
+    dev = W.device
+    data = torch.empty(max(packed_weight_bytes(N, K), 16), dtype=torch.uint8, device=dev)
+    scale = torch.empty(max(N, 1), dtype=torch.float32, device=dev)
+    ws_bytes = pack_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError("workspace too small")
+    if group_rows is None:
+        groups, ngroups = 0, 0
+    else:
+        arr = (ctypes.c_int64 * len(group_rows))(*[int(r) for r in group_rows])
+        groups, ngroups = ctypes.cast(arr, ctypes.c_void_p).value, len(group_rows)
+    check(lib().bt_pack_weights_rows(_ptr(W), N, K, groups, ngroups, _ptr(data), _ptr(scale), _ptr(workspace),
+                                     _stream(dev)))
+    return PackedWeight(data, scale, N, K, row_scales=True)
 
 
 def unpack_weights(pw: PackedWeight) -> torch.Tensor:
@@ -110,8 +135,10 @@ def _product(fn_name, pw: PackedWeight, q, want_y, want_acc, out_y, out_acc, alg
 
 
 def ternary_gemv(pw: PackedWeight, q, want_y=True, want_acc=False, out_y=None, out_acc=None, algo=GEMV_AUTO):
-    """bt_ternary_gemv_algo: decode product for M <= 16 tokens. Returns (Y, acc)."""
-    return _product("bt_ternary_gemv_algo", pw, q, want_y, want_acc, out_y, out_acc, algo)
+    """bt_ternary_gemv_algo (bt_ternary_gemv_rs for row scales): decode product for M <= 16
+    tokens. Returns (Y, acc)."""
+    fn = "bt_ternary_gemv_rs" if pw.row_scales else "bt_ternary_gemv_algo"
+    return _product(fn, pw, q, want_y, want_acc, out_y, out_acc, algo)
 
 
 def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
@@ -132,11 +159,11 @@ def ternary_gemm(pw: PackedWeight, q, want_y=True, want_acc=False, out_y=None, o
     With a workspace (see gemm_workspace) the call is bt_ternary_gemm_ws, which splits K
     over several workgroups per tile where that pays; results are identical.
     """
-    if workspace is None:
+    if workspace is None and not pw.row_scales:
         return _product("bt_ternary_gemm", pw, q, want_y, want_acc, out_y, out_acc)
-    nbytes = workspace.numel() * workspace.element_size()
-    return _product("bt_ternary_gemm_ws", pw, q, want_y, want_acc, out_y, out_acc,
-                    extra=(_ptr(workspace), nbytes))
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return _product("bt_ternary_gemm_rs" if pw.row_scales else "bt_ternary_gemm_ws", pw, q, want_y, want_acc,
+                    out_y, out_acc, extra=(_ptr(workspace), nbytes))
 
 
 def linear_workspace_bytes(M: int, N: int, K: int) -> int:
@@ -161,6 +188,7 @@ def linear(X: torch.Tensor, pw: PackedWeight, want_y=True, want_acc=False, out_y
     ws_bytes = linear_workspace_bytes(M, pw.N, K)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    check(lib().bt_ternary_linear(_ptr(pw.data), _ptr(pw.scale), _ptr(X), M, pw.N, K, _ptr(Y), _ptr(acc),
-                                  _ptr(workspace) if ws_bytes else 0, _stream(dev)))
+    fn = lib().bt_ternary_linear_rs if pw.row_scales else lib().bt_ternary_linear
+    check(fn(_ptr(pw.data), _ptr(pw.scale), _ptr(X), M, pw.N, K, _ptr(Y), _ptr(acc),
+             _ptr(workspace) if ws_bytes else 0, _stream(dev)))
     return Y, acc

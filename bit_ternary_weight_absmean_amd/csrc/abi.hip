@@ -112,6 +112,46 @@ bt_status bt_pack_weights(const float *W, int64_t N, int64_t K, void *Wp, float 
                       "bt_pack_weights launch");
 }
 
+bt_status bt_pack_weights_rows(const float *W, int64_t N, int64_t K, const int64_t *group_rows, int64_t ngroups,
+                               void *Wp, float *row_scale, void *workspace, void *stream)
+{
+    if (N < 0 || N > (int64_t)1 << 30)
+        return fail(BT_ERR_SHAPE, "N = %lld outside [0, 2^30]", (long long)N);
+    if (bt_status s = check_k(K))
+        return s;
+    bt::RowGroups groups{};
+    if (group_rows) {
+        if (ngroups < 1 || ngroups > BT_MAX_ROW_GROUPS)
+            return fail(BT_ERR_SHAPE, "ngroups = %lld outside [1, %d]", (long long)ngroups, BT_MAX_ROW_GROUPS);
+        int64_t end = 0;
+        for (int64_t g = 0; g < ngroups; ++g) {
+            if (group_rows[g] < 1)
+                return fail(BT_ERR_SHAPE, "group %lld has %lld rows", (long long)g, (long long)group_rows[g]);
+            end += group_rows[g];
+            if (end > N)
+                break;
+            groups.end[g] = end;
+        }
+        if (end != N)
+            return fail(BT_ERR_SHAPE, "the row groups cover %lld rows, not N = %lld", (long long)end, (long long)N);
+        groups.n = (int)ngroups;
+    }
+    if (N == 0)
+        return ok();
+    if (!W && K > 0)
+        return fail(BT_ERR_NULL, "NULL W");
+    if (!row_scale || (K > 0 && (!Wp || !workspace)))
+        return fail(BT_ERR_NULL, "NULL Wp, row_scale or workspace");
+    if ((W && !aligned(W, 16)) || (Wp && !aligned(Wp, 16)))
+        return fail(BT_ERR_ALIGN, "W and Wp must be 16-byte aligned");
+    if (!aligned(row_scale, 4) || (workspace && !aligned(workspace, 8)))
+        return fail(BT_ERR_ALIGN, "row_scale must be 4-byte aligned, workspace 8-byte aligned");
+    return hip_status(bt::launch_pack_rows(W, N, K, group_rows ? &groups : nullptr, static_cast<uint4 *>(Wp),
+                                           row_scale, static_cast<double *>(workspace),
+                                           static_cast<hipStream_t>(stream)),
+                      "bt_pack_weights_rows launch");
+}
+
 bt_status bt_unpack_weights(const void *Wp, int64_t N, int64_t K, int8_t *T, void *stream)
 {
     if (N < 0 || N > (int64_t)1 << 30)
@@ -148,9 +188,12 @@ bt_status bt_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *
                       "bt_quant_act launch");
 }
 
-bt_status bt_ternary_gemv_algo(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
-                               const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
-                               int32_t algo, void *stream)
+// The products and the linear layer, with the weight scale as w_scale[0] (rows false)
+// or one scale per output row, w_scale[n] (rows true). The row-scale array needs the same
+// 4-byte alignment; its N entries are not otherwise checked.
+static bt_status gemv_impl(const void *Wp, const float *w_scale, bool rows, const int8_t *Xq, const float *x_scale,
+                           const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                           int32_t algo, void *stream)
 {
     if (bt_status s = check_product(Wp, w_scale, Xq, x_scale, x_sum, M, N, K, Y, acc))
         return s;
@@ -169,27 +212,14 @@ bt_status bt_ternary_gemv_algo(const void *Wp, const float *w_scale, const int8_
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const uint4 *W = static_cast<const uint4 *>(Wp);
     hipError_t e = (algo == BT_GEMV_DOT4)
-                       ? bt::launch_gemv_dot4(W, w_scale, Xq, ldq, x_scale, x_sum, M, N, K, Y, acc, s)
-                       : bt::launch_gemv_mfma(W, w_scale, Xq, ldq, x_scale, x_sum, M, N, K, Y, acc, s);
+                       ? bt::launch_gemv_dot4(W, w_scale, rows, Xq, ldq, x_scale, x_sum, M, N, K, Y, acc, s)
+                       : bt::launch_gemv_mfma(W, w_scale, rows, Xq, ldq, x_scale, x_sum, M, N, K, Y, acc, s);
     return hip_status(e, "bt_ternary_gemv launch");
 }
 
-bt_status bt_ternary_gemv(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
-                          const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *stream)
-{
-    return bt_ternary_gemv_algo(Wp, w_scale, Xq, x_scale, x_sum, M, N, K, Y, acc, BT_GEMV_AUTO, stream);
-}
-
-size_t bt_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
-{
-    if (M <= 0 || N <= 0 || K <= 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > BT_MAX_K)
-        return 0;
-    return bt::gemm_workspace_bytes(M, N, K);
-}
-
-bt_status bt_ternary_gemm_ws(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
-                             const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
-                             void *workspace, size_t workspace_bytes, void *stream)
+static bt_status gemm_impl(const void *Wp, const float *w_scale, bool rows, const int8_t *Xq, const float *x_scale,
+                           const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                           void *workspace, size_t workspace_bytes, void *stream)
 {
     if (bt_status s = check_product(Wp, w_scale, Xq, x_scale, x_sum, M, N, K, Y, acc))
         return s;
@@ -198,16 +228,10 @@ bt_status bt_ternary_gemm_ws(const void *Wp, const float *w_scale, const int8_t 
     if (M == 0 || N == 0)
         return ok();
     const int64_t ldq = bt_act_row_bytes(K);
-    return hip_status(bt::launch_gemm(static_cast<const uint4 *>(Wp), w_scale, Xq, ldq, x_scale, x_sum, M, N, K, Y,
-                                      acc, workspace, workspace ? workspace_bytes : 0,
+    return hip_status(bt::launch_gemm(static_cast<const uint4 *>(Wp), w_scale, rows, Xq, ldq, x_scale, x_sum, M, N,
+                                      K, Y, acc, workspace, workspace ? workspace_bytes : 0,
                                       static_cast<hipStream_t>(stream)),
                       "bt_ternary_gemm launch");
-}
-
-bt_status bt_ternary_gemm(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
-                          const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *stream)
-{
-    return bt_ternary_gemm_ws(Wp, w_scale, Xq, x_scale, x_sum, M, N, K, Y, acc, nullptr, 0, stream);
 }
 
 // Largest LDS footprint the fused decode kernel is launched with.
@@ -229,16 +253,8 @@ static size_t linear_quant_bytes(int64_t M, int64_t K)
     return (size_t)(bt::round_up(M * bt_act_row_bytes(K), 256) + 2 * bt::round_up(4 * M, 256));
 }
 
-size_t bt_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
-{
-    if (M <= 0 || N <= 0 || K < 0 || linear_fused(M, N, K))
-        return 0;
-    const size_t gemm = M > BT_GEMV_MAX_M ? bt_gemm_workspace_bytes(M, N, K) : 0;
-    return linear_quant_bytes(M, K) + gemm;
-}
-
-bt_status bt_ternary_linear(const void *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
-                            float *Y, int32_t *acc, void *workspace, void *stream)
+static bt_status linear_impl(const void *Wp, const float *w_scale, bool rows, const float *X, int64_t M, int64_t N,
+                             int64_t K, float *Y, int32_t *acc, void *workspace, void *stream)
 {
     if (M < 0 || N < 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30)
         return fail(BT_ERR_SHAPE, "shape M = %lld, N = %lld out of range", (long long)M, (long long)N);
@@ -255,8 +271,9 @@ bt_status bt_ternary_linear(const void *Wp, const float *w_scale, const float *X
         return fail(BT_ERR_ALIGN, "Wp must be 16-byte aligned; X, w_scale, Y and acc 4-byte aligned");
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (linear_fused(M, N, K))
-        return hip_status(bt::launch_linear_decode(static_cast<const uint4 *>(Wp), w_scale, X, M, N, K, Y, acc, s),
-                          "bt_ternary_linear launch");
+        return hip_status(
+            bt::launch_linear_decode(static_cast<const uint4 *>(Wp), w_scale, rows, X, M, N, K, Y, acc, s),
+            "bt_ternary_linear launch");
     if (!workspace)
         return fail(BT_ERR_NULL, "workspace is NULL but bt_linear_workspace_bytes(%lld, %lld, %lld) = %zu",
                     (long long)M, (long long)N, (long long)K, bt_linear_workspace_bytes(M, N, K));
@@ -268,7 +285,7 @@ bt_status bt_ternary_linear(const void *Wp, const float *w_scale, const float *X
     if (M <= BT_GEMV_MAX_M) {
         if (bt_status st = bt_quant_act(X, M, K, Xq, sx, xsum, stream))
             return st;
-        return bt_ternary_gemv_algo(Wp, w_scale, Xq, sx, xsum, M, N, K, Y, acc, BT_GEMV_MFMA, stream);
+        return gemv_impl(Wp, w_scale, rows, Xq, sx, xsum, M, N, K, Y, acc, BT_GEMV_MFMA, stream);
     }
     // The quantizer also zero-fills the split-K arrival counters of the GEMM workspace,
     // so the caller's workspace needs no initialization.
@@ -279,7 +296,74 @@ bt_status bt_ternary_linear(const void *Wp, const float *w_scale, const float *X
                                                        gbytes ? bt::gemm_arrival_words(M, N) : 0, s),
                                   "bt_quant_act launch"))
         return st;
-    return bt_ternary_gemm_ws(Wp, w_scale, Xq, sx, xsum, M, N, K, Y, acc, gbytes ? gws : nullptr, gbytes, stream);
+    return gemm_impl(Wp, w_scale, rows, Xq, sx, xsum, M, N, K, Y, acc, gbytes ? gws : nullptr, gbytes, stream);
+}
+
+bt_status bt_ternary_gemv_algo(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
+                               const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                               int32_t algo, void *stream)
+{
+    return gemv_impl(Wp, w_scale, false, Xq, x_scale, x_sum, M, N, K, Y, acc, algo, stream);
+}
+
+bt_status bt_ternary_gemv(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
+                          const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *stream)
+{
+    return gemv_impl(Wp, w_scale, false, Xq, x_scale, x_sum, M, N, K, Y, acc, BT_GEMV_AUTO, stream);
+}
+
+bt_status bt_ternary_gemv_rs(const void *Wp, const float *row_scale, const int8_t *Xq, const float *x_scale,
+                             const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                             int32_t algo, void *stream)
+{
+    return gemv_impl(Wp, row_scale, true, Xq, x_scale, x_sum, M, N, K, Y, acc, algo, stream);
+}
+
+size_t bt_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > BT_MAX_K)
+        return 0;
+    return bt::gemm_workspace_bytes(M, N, K);
+}
+
+bt_status bt_ternary_gemm_ws(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
+                             const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    return gemm_impl(Wp, w_scale, false, Xq, x_scale, x_sum, M, N, K, Y, acc, workspace, workspace_bytes, stream);
+}
+
+bt_status bt_ternary_gemm(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
+                          const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *stream)
+{
+    return gemm_impl(Wp, w_scale, false, Xq, x_scale, x_sum, M, N, K, Y, acc, nullptr, 0, stream);
+}
+
+bt_status bt_ternary_gemm_rs(const void *Wp, const float *row_scale, const int8_t *Xq, const float *x_scale,
+                             const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    return gemm_impl(Wp, row_scale, true, Xq, x_scale, x_sum, M, N, K, Y, acc, workspace, workspace_bytes, stream);
+}
+
+size_t bt_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K < 0 || linear_fused(M, N, K))
+        return 0;
+    const size_t gemm = M > BT_GEMV_MAX_M ? bt_gemm_workspace_bytes(M, N, K) : 0;
+    return linear_quant_bytes(M, K) + gemm;
+}
+
+bt_status bt_ternary_linear(const void *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+                            float *Y, int32_t *acc, void *workspace, void *stream)
+{
+    return linear_impl(Wp, w_scale, false, X, M, N, K, Y, acc, workspace, stream);
+}
+
+bt_status bt_ternary_linear_rs(const void *Wp, const float *row_scale, const float *X, int64_t M, int64_t N,
+                               int64_t K, float *Y, int32_t *acc, void *workspace, void *stream)
+{
+    return linear_impl(Wp, row_scale, true, X, M, N, K, Y, acc, workspace, stream);
 }
 
 const char *bt_status_str(bt_status s)

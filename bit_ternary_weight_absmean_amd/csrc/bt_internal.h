@@ -37,23 +37,35 @@ __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + 
 // Wave-uniform value the compiler can keep in an SGPR.
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Row groups of bt_pack_weights_rows: group g covers rows end[g-1] .. end[g]-1 (end[-1] = 0).
+constexpr int kMaxRowGroups = 8;
+struct RowGroups {
+    int64_t end[kMaxRowGroups];
+    int n;
+};
+
 // Launchers (each returns hipGetLastError() after the launch).
 hipError_t launch_pack(const float *W, int64_t N, int64_t K, uint4 *Wp, float *gamma, double *rowsum,
                        hipStream_t s);
+// Row-group scales into row_scale[N]; groups == NULL: one group per row.
+hipError_t launch_pack_rows(const float *W, int64_t N, int64_t K, const RowGroups *groups, uint4 *Wp,
+                            float *row_scale, double *rowsum, hipStream_t s);
 hipError_t launch_unpack(const uint4 *Wp, int64_t N, int64_t K, int8_t *T, hipStream_t s);
 // The quantizer also zero-fills `clear_words` 32-bit words at `clear` (split-K arrival
 // counters of the product that follows it; NULL / 0 for none).
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int64_t ldq, int8_t *Xq, float *sx,
                             int32_t *xsum, unsigned *clear, int64_t clear_words, hipStream_t s);
-hipError_t launch_gemv_dot4(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq,
+// The product launchers take the weight scale as w_scale[0] (row_scales false) or as
+// one scale per output row, w_scale[n] (row_scales true).
+hipError_t launch_gemv_dot4(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq,
                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
                             int32_t *acc, hipStream_t s);
-hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq,
+hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq,
                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
                             int32_t *acc, hipStream_t s);
 // Fused decode (quantize + product + epilogue) for M <= 4; LDS bytes it needs.
-hipError_t launch_linear_decode(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N,
-                                int64_t K, float *Y, int32_t *acc, hipStream_t s);
+hipError_t launch_linear_decode(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M,
+                                int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s);
 size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K);
 // Prefill GEMM. With a workspace of at least gemm_workspace_bytes(M, N, K) bytes whose
 // first gemm_arrival_words(M, N) words are zero, shapes that gain from it split K over
@@ -62,8 +74,8 @@ size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K);
 int gemm_splits(int64_t M, int64_t N, int64_t K);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int64_t gemm_arrival_words(int64_t M, int64_t N);
-hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
-                       const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *workspace,
-                       size_t workspace_bytes, hipStream_t s);
+hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq,
+                       const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                       void *workspace, size_t workspace_bytes, hipStream_t s);
 
 }  // namespace bt

@@ -137,9 +137,10 @@ __device__ inline int lds_x_offset(int k4) { return (k4 >> 4) * 64 + 16 * (k4 & 
 
 // Partial accumulators of all waves -> y and acc. red[w][k][v][lane]; o = m * rows + nl.
 // token_stats(m, qs, sx) supplies sum_k q and s_x of token m.
+// w_scale[rs ? n : 0] is the weight scale of output row n.
 template <int WAVES, int RB, typename Stats>
-__device__ inline void epilogue(const int *red, int tid, int M, int64_t N, float gamma, Stats token_stats,
-                                float *__restrict__ Y, int32_t *__restrict__ ACC)
+__device__ inline void epilogue(const int *red, int tid, int M, int64_t N, const float *__restrict__ w_scale, int rs,
+                                Stats token_stats, float *__restrict__ Y, int32_t *__restrict__ ACC)
 {
     constexpr int rows = 16 * RB;
     for (int o = tid; o < M * rows; o += WAVES * 64) {
@@ -161,7 +162,7 @@ __device__ inline void epilogue(const int *red, int tid, int M, int64_t N, float
         if (ACC)
             ACC[(int64_t)m * N + n] = acc;
         if (Y)
-            Y[(int64_t)m * N + n] = (float)acc * (gamma * sxm);
+            Y[(int64_t)m * N + n] = (float)acc * (w_scale[rs ? n : 0] * sxm);
     }
 }
 
@@ -173,7 +174,7 @@ template <int RB>
 __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
     const float *__restrict__ sx_in, const int32_t *__restrict__ xsum_in, int M, int64_t N, int KC, int NB16,
-    float *__restrict__ Y, int32_t *__restrict__ ACC)
+    float *__restrict__ Y, int32_t *__restrict__ ACC, int rs)
 {
     constexpr int WAVES = kDirectWaves;
     constexpr int U = 2;
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct(
         for (int v = 0; v < 4; ++v)
             red[((wave * RB + k) * 4 + v) * 64 + lane] = a1[k][v] + (a4[k][v] >> 2) + (a16[k][v] >> 4);
     __syncthreads();
-    epilogue<WAVES, RB>(red, tid, M, N, w_scale[0],
+    epilogue<WAVES, RB>(red, tid, M, N, w_scale, rs,
                         [&](int m, int &qs, float &sxm) {
                             qs = xsum_in[m];
                             sxm = sx_in[m];
@@ -253,7 +254,7 @@ template <int RB, int U>
 __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct_db(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
     const float *__restrict__ sx_in, const int32_t *__restrict__ xsum_in, int M, int64_t N, int KC, int NB16,
-    float *__restrict__ Y, int32_t *__restrict__ ACC)
+    float *__restrict__ Y, int32_t *__restrict__ ACC, int rs)
 {
     constexpr int WAVES = kDirectWaves;
     __shared__ int red[WAVES * RB * 256];
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct_db(
         for (int v = 0; v < 4; ++v)
             red[((wave * RB + k) * 4 + v) * 64 + lane] = a1[k][v] + (a4[k][v] >> 2) + (a16[k][v] >> 4);
     __syncthreads();
-    epilogue<WAVES, RB>(red, tid, M, N, w_scale[0],
+    epilogue<WAVES, RB>(red, tid, M, N, w_scale, rs,
                         [&](int m, int &qs, float &sxm) {
                             qs = xsum_in[m];
                             sxm = sx_in[m];
@@ -358,13 +359,14 @@ __host__ __device__ constexpr int fused_pitch(int KC4, int rx)
 // launch's critical path (at 2B sizes the weights are in registers well before the
 // quantizer is done), and a SIMD runs two of the eight waves: the work that does not
 // need the token maxima is done before or after the two barriers around the quantizer.
-template <int MT, int S, int RX, int U>
+template <int MT, int S, int RX, int U, bool ROWS>
 __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const float *__restrict__ X,
     float *__restrict__ Y, int32_t *__restrict__ ACC, int M, int N, int K)
 {
     // The arguments fill the 13 dwords gfx950 preloads into SGPRs, so no scalar load of
-    // the kernel arguments is pending at the first barrier.
+    // the kernel arguments is pending at the first barrier. ROWS: w_scale holds one scale
+    // per output row (else w_scale[0] is the matrix's scale: one load instead of four).
     constexpr int WAVES = kFusedWaves;
     static_assert(WAVES == 8, "the token maxima are read as two float4");
     const int KC = (K + 63) >> 6;
@@ -446,7 +448,14 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
             load_batch(wb, 1);
     }
     // After the weights: the epilogue is the only user, and it waits for them anyway.
-    const float gamma = load_scale_vmem(w_scale);
+    // Lane (g, r) stores rows 4g .. 4g+3 of its block.
+    float4 gam;
+    if constexpr (ROWS) {
+        gam = load_scales4(w_scale, (int64_t)b16 * 16 + 4 * g, N, true);
+    } else {
+        const float g1 = load_scale_vmem(w_scale);
+        gam = make_float4(g1, g1, g1, g1);
+    }
 
     // 3. Per-token absmax: wave partials in LDS.
     float4 xr[MT][RPT];
@@ -625,9 +634,11 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     }
     // The epilogue wave's scale, formed before it waits for the other k-splits (it owns
     // the fewest steps, so it reaches the barrier first).
-    float scale = 0.0f;
-    if (ks == KE)
-        scale = gamma * ((amax_r == 0.0f) ? 0.0f : amax_r / 127.0f);
+    float4 scale = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (ks == KE) {
+        const float sx = (amax_r == 0.0f) ? 0.0f : amax_r / 127.0f;
+        scale = make_float4(gam.x * sx, gam.y * sx, gam.z * sx, gam.w * sx);
+    }
     if constexpr (S > 1) {
         if (ks != KE)
             red[wave * 64 + lane] = make_int4(part[0], part[1], part[2], part[3]);
@@ -654,9 +665,10 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
             if (ACC)
                 *reinterpret_cast<int4 *>(ACC + (int64_t)r * N + n0) = acc;
             if (Y)
-                *reinterpret_cast<float4 *>(Y + (int64_t)r * N + n0) =
-                    make_float4((float)acc.x * scale, (float)acc.y * scale, (float)acc.z * scale, (float)acc.w * scale);
+                *reinterpret_cast<float4 *>(Y + (int64_t)r * N + n0) = make_float4(
+                    (float)acc.x * scale.x, (float)acc.y * scale.y, (float)acc.z * scale.z, (float)acc.w * scale.w);
         } else {
+            const float sc[4] = {scale.x, scale.y, scale.z, scale.w};
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int64_t n = n0 + v;
@@ -665,7 +677,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
                     if (ACC)
                         ACC[(int64_t)r * N + n] = acc;
                     if (Y)
-                        Y[(int64_t)r * N + n] = (float)acc * scale;
+                        Y[(int64_t)r * N + n] = (float)acc * sc[v];
                 }
             }
         }
@@ -722,38 +734,42 @@ int fused_rx(int64_t M, int64_t K)
 }
 
 template <int MT, int S, int RX, int U>
-hipError_t launch_fused_u(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+hipError_t launch_fused_u(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M, int64_t N, int64_t K,
                           float *Y, int32_t *acc, hipStream_t s)
 {
     constexpr int RBW = kFusedWaves / S;
     const int64_t nb16 = (N + 15) / 16;
     const dim3 grid((unsigned)((nb16 + RBW - 1) / RBW)), block(kFusedWaves * 64);
-    hipLaunchKernelGGL((k_linear_decode<MT, S, RX, U>), grid, block, fused_lds(M, K, S, RX), s, Wp, w_scale, X, Y, acc,
-                       (int)M, (int)N, (int)K);
+    if (row_scales)
+        hipLaunchKernelGGL((k_linear_decode<MT, S, RX, U, true>), grid, block, fused_lds(M, K, S, RX), s, Wp, w_scale,
+                           X, Y, acc, (int)M, (int)N, (int)K);
+    else
+        hipLaunchKernelGGL((k_linear_decode<MT, S, RX, U, false>), grid, block, fused_lds(M, K, S, RX), s, Wp, w_scale,
+                           X, Y, acc, (int)M, (int)N, (int)K);
     return hipGetLastError();
 }
 
 // Batch size: the steps of 256 k a wave owns (at most ceil(steps / S)) over two batches.
 template <int MT, int S, int RX>
-hipError_t launch_fused_rx(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+hipError_t launch_fused_rx(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M, int64_t N, int64_t K,
                            float *Y, int32_t *acc, hipStream_t s)
 {
     const int64_t steps = (K + 255) / 256;
     const int64_t mine = (steps + S - 1) / S;
     if (mine <= 2)
-        return launch_fused_u<MT, S, RX, 1>(Wp, w_scale, X, M, N, K, Y, acc, s);
+        return launch_fused_u<MT, S, RX, 1>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
     if (mine <= 4)
-        return launch_fused_u<MT, S, RX, 2>(Wp, w_scale, X, M, N, K, Y, acc, s);
+        return launch_fused_u<MT, S, RX, 2>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
     if (mine <= 6)
-        return launch_fused_u<MT, S, RX, 3>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    return launch_fused_u<MT, S, RX, 4>(Wp, w_scale, X, M, N, K, Y, acc, s);
+        return launch_fused_u<MT, S, RX, 3>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    return launch_fused_u<MT, S, RX, 4>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
 }
 
 // Register path when the rows are 16-byte aligned with K % 4 == 0 and each thread's
 // share fits kXRegs float4 over all MT tokens: RX = the smallest power of two with
 // RX * 512 >= K / 4.
 template <int MT, int S>
-hipError_t launch_fused_t(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+hipError_t launch_fused_t(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M, int64_t N, int64_t K,
                           float *Y, int32_t *acc, hipStream_t s)
 {
     const int64_t K4 = K / 4, T = kFusedWaves * 64;
@@ -762,30 +778,30 @@ hipError_t launch_fused_t(const uint4 *Wp, const float *w_scale, const float *X,
     while ((int64_t)rx * T < K4)
         rx *= 2;
     if (!vec || rx * MT > kXRegs)
-        return launch_fused_rx<MT, S, 0>(Wp, w_scale, X, M, N, K, Y, acc, s);
+        return launch_fused_rx<MT, S, 0>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
     switch (rx) {
-    case 1: return launch_fused_rx<MT, S, 1>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    case 2: return launch_fused_rx<MT, S, (MT <= 8 ? 2 : 1)>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    case 4: return launch_fused_rx<MT, S, (MT <= 4 ? 4 : 1)>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    case 8: return launch_fused_rx<MT, S, (MT <= 2 ? 8 : 1)>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    default: return launch_fused_rx<MT, S, (MT <= 1 ? 16 : 1)>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    case 1: return launch_fused_rx<MT, S, 1>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 2: return launch_fused_rx<MT, S, (MT <= 8 ? 2 : 1)>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 4: return launch_fused_rx<MT, S, (MT <= 4 ? 4 : 1)>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 8: return launch_fused_rx<MT, S, (MT <= 2 ? 8 : 1)>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    default: return launch_fused_rx<MT, S, (MT <= 1 ? 16 : 1)>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
     }
 }
 
 template <int MT>
-hipError_t launch_fused_mt(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N, int64_t K,
+hipError_t launch_fused_mt(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M, int64_t N, int64_t K,
                            float *Y, int32_t *acc, hipStream_t s)
 {
     switch (pick_s(N)) {
-    case 1: return launch_fused_t<MT, 1>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    case 2: return launch_fused_t<MT, 2>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    case 4: return launch_fused_t<MT, 4>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    default: return launch_fused_t<MT, 8>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    case 1: return launch_fused_t<MT, 1>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 2: return launch_fused_t<MT, 2>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 4: return launch_fused_t<MT, 4>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    default: return launch_fused_t<MT, 8>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
     }
 }
 
 template <int RB>
-hipError_t launch_direct_t(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
+hipError_t launch_direct_t(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq, const float *sx,
                            const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
                            hipStream_t s)
 {
@@ -798,13 +814,13 @@ hipError_t launch_direct_t(const uint4 *Wp, const float *w_scale, const int8_t *
     const int64_t mine = ((K + 255) / 256 + kDirectWaves - 1) / kDirectWaves;
     if (RB > 1)
         hipLaunchKernelGGL((k_gemv_direct<RB>), grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, NB16, Y,
-                           acc);
+                           acc, (int)row_scales);
     else if (mine <= 2)
         hipLaunchKernelGGL((k_gemv_direct_db<RB, 1>), grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M,
-                           N, KC, NB16, Y, acc);
+                           N, KC, NB16, Y, acc, (int)row_scales);
     else
         hipLaunchKernelGGL((k_gemv_direct_db<RB, 2>), grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M,
-                           N, KC, NB16, Y, acc);
+                           N, KC, NB16, Y, acc, (int)row_scales);
     return hipGetLastError();
 }
 
@@ -813,26 +829,26 @@ hipError_t launch_direct_t(const uint4 *Wp, const float *w_scale, const int8_t *
 // An upper bound for any activation alignment: the register path's pitch is the larger.
 size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K) { return fused_lds(M, K, pick_s(N), fused_rx(M, K)); }
 
-hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq,
+hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq,
                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
                             int32_t *acc, hipStream_t s)
 {
     switch (pick_rb(N)) {
-    case 4: return launch_direct_t<4>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
-    case 2: return launch_direct_t<2>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
-    default: return launch_direct_t<1>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    case 4: return launch_direct_t<4>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    case 2: return launch_direct_t<2>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    default: return launch_direct_t<1>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
     }
 }
 
-hipError_t launch_linear_decode(const uint4 *Wp, const float *w_scale, const float *X, int64_t M, int64_t N,
+hipError_t launch_linear_decode(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M, int64_t N,
                                 int64_t K, float *Y, int32_t *acc, hipStream_t s)
 {
     if (M > 4)
         return hipErrorInvalidValue;
     switch (pick_mt(M)) {
-    case 1: return launch_fused_mt<1>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    case 2: return launch_fused_mt<2>(Wp, w_scale, X, M, N, K, Y, acc, s);
-    default: return launch_fused_mt<4>(Wp, w_scale, X, M, N, K, Y, acc, s);
+    case 1: return launch_fused_mt<1>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 2: return launch_fused_mt<2>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    default: return launch_fused_mt<4>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
     }
 }
 

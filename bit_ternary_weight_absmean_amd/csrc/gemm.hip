@@ -96,9 +96,12 @@ template <int BM, int BN, int WM, int WN, int NS, int WPE, int SPLIT>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void k_gemm(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
     const float *__restrict__ sx, const int32_t *__restrict__ xsum, int64_t M, int64_t N, int KC, int NBLK,
-    int tiles_m, int tiles_n, int group, float *__restrict__ Y, int32_t *__restrict__ ACC, int vec,
+    int tiles_m, int tiles_n, int group, float *__restrict__ Y, int32_t *__restrict__ ACC, int flags,
     char *__restrict__ partials, unsigned *__restrict__ arrivals, int per_xcd)
 {
+    // flags bit 0: 16-byte output stores; bit 1: w_scale holds one scale per output row.
+    const int vec = flags & 1;
+    const bool rows = (flags & 2) != 0;
     using C = GemmCfg<BM, BN, WM, WN, NS>;
     constexpr int TM = C::TM, TN = C::TN;
     // One LDS array per ring stage ([A tile | B tile] each): distinct objects let the
@@ -155,17 +158,22 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     const int rb0 = tn * (BN / 64);  // first 64-row weight block of the workgroup
 
     // The epilogue's inputs, requested now so that their round trip overlaps the main loop
-    // instead of following it: gamma, and the row statistics of the workgroup's BM rows
+    // instead of following it: the weight scales of the workgroup's BN output columns
+    // (thread t holds column t's, clamped: the scale array or the one matrix scale), and
+    // the row statistics of the workgroup's BM rows
     // (thread t holds row m0 + t % BM, clamped; every thread loads, so the loads need no
     // branch). The first BM threads park them in LDS once the prologue's wait has retired
     // them (they are older than every operand load).
+    static_assert(BN == C::kThreads, "one column scale per thread");
     __shared__ int32_t s_xsum[BM];
     __shared__ float s_sx[BM];
-    const float gamma = w_scale[0];
+    __shared__ __attribute__((aligned(16))) float s_gam[BN];
+    const float gam_t = w_scale[rows ? min((int64_t)tn * BN + tid, N - 1) : 0];
     const int64_t m_stat = min(m0 + tid % BM, M - 1);
     const int32_t xsum_t = xsum[m_stat];
     const float sx_t = sx[m_stat];
     auto park_stats = [&] {
+        s_gam[tid] = gam_t;
         if (tid < BM) {
             s_xsum[tid] = xsum_t;
             s_sx[tid] = sx_t;
@@ -387,7 +395,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     constexpr int kHalf = C::kWaves / 2;
     int32_t *slab = reinterpret_cast<int32_t *>(wave < kHalf ? lds0 : lds1) + (wave % kHalf) * 16 * kPitchW;
     const int64_t n0 = (int64_t)tn * BN + wn * 64;
-    // Row statistics of the lane's 16 rows, from LDS.
+    // Weight scales of the lane's columns (n0 + 4r .. +3 when vec, n0 + lane otherwise) and
+    // row statistics of the lane's 16 rows, from LDS.
+    const float4 gam = vec ? *reinterpret_cast<const float4 *>(s_gam + wn * 64 + 4 * r)
+                           : make_float4(s_gam[wn * 64 + lane], 0.0f, 0.0f, 0.0f);
     int32_t xs_r[TM * 4];
     float sx_r[TM * 4];
 #pragma unroll
@@ -413,15 +424,15 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
                 const v4i a4 = *reinterpret_cast<const v4i *>(slab + rr * kPitchW + 4 * r);
                 if (m < M && n < N) {
                     const int32_t xs_m = xs_r[4 * a + q];
-                    const float scale = gamma * sx_r[4 * a + q];
+                    const float sxm = sx_r[4 * a + q];
                     const v4i d = a4 - xs_m;
                     // Non-temporal: the output is not read again by this kernel, and
                     // streaming it past the caches measured 3-9% faster here.
                     if (ACC)
                         __builtin_nontemporal_store(d, reinterpret_cast<v4i *>(ACC + m * N + n));
                     if (Y) {
-                        const v4f y = {(float)d[0] * scale, (float)d[1] * scale, (float)d[2] * scale,
-                                       (float)d[3] * scale};
+                        const v4f y = {(float)d[0] * (gam.x * sxm), (float)d[1] * (gam.y * sxm),
+                                       (float)d[2] * (gam.z * sxm), (float)d[3] * (gam.w * sxm)};
                         __builtin_nontemporal_store(y, reinterpret_cast<v4f *>(Y + m * N + n));
                     }
                 }
@@ -436,7 +447,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
                     if (ACC)
                         __builtin_nontemporal_store(d, ACC + m * N + n);
                     if (Y)
-                        __builtin_nontemporal_store((float)d * (gamma * sx[m]), Y + m * N + n);
+                        __builtin_nontemporal_store((float)d * (gam.x * sx[m]), Y + m * N + n);
                 }
             }
         }
@@ -444,7 +455,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int WPE, int SPLIT>
-hipError_t launch_t(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
+hipError_t launch_t(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq, const float *sx,
                     const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, char *partials,
                     unsigned *arrivals, hipStream_t s)
 {
@@ -459,7 +470,8 @@ hipError_t launch_t(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int
     const int vec = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(acc) % 16 == 0);
     hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, WPE, SPLIT>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0,
-                       s, Wp, w_scale, Xq, ldq, sx, xsum, M, N, KC, NBLK, tiles_m, tiles_n, kGroup, Y, acc, vec,
+                       s, Wp, w_scale, Xq, ldq, sx, xsum, M, N, KC, NBLK, tiles_m, tiles_n, kGroup, Y, acc,
+                       vec | (row_scales ? 2 : 0),
                        partials, arrivals, per_xcd);
     return hipGetLastError();
 }
@@ -494,7 +506,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
     return (size_t)(round_up(4 * tiles, 256) + tiles * S * (int64_t)kPartialBytes<kBM, kBN>);
 }
 
-hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq, const float *sx,
+hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq, const float *sx,
                        const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *workspace,
                        size_t workspace_bytes, hipStream_t s)
 {
@@ -506,14 +518,14 @@ hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, const int8_t *Xq, 
     const int S = gemm_splits(M, N, K);
     const size_t need = gemm_workspace_bytes(M, N, K);
     if (S == 1 || !workspace || workspace_bytes < need)
-        return launch_t<kBM, kBN, 1, 4, 3, 3, 1>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, nullptr, nullptr, s);
+        return launch_t<kBM, kBN, 1, 4, 3, 3, 1>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, nullptr, nullptr, s);
     unsigned *arrivals = static_cast<unsigned *>(workspace);
     char *partials = static_cast<char *>(workspace) + round_up(4 * gemm_tiles(M, N), 256);
     if (S == 2)
-        return launch_t<kBM, kBN, 1, 4, 3, 3, 2>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
+        return launch_t<kBM, kBN, 1, 4, 3, 3, 2>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
     if (S == 3)
-        return launch_t<kBM, kBN, 1, 4, 3, 3, 3>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
-    return launch_t<kBM, kBN, 1, 4, 3, 3, 4>(Wp, w_scale, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
+        return launch_t<kBM, kBN, 1, 4, 3, 3, 3>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
+    return launch_t<kBM, kBN, 1, 4, 3, 3, 4>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
 }
 
 int64_t gemm_arrival_words(int64_t M, int64_t N) { return gemm_tiles(M, N); }

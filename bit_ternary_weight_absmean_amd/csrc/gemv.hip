@@ -28,7 +28,7 @@ template <int MT>
 __global__ __launch_bounds__(kDot4Waves * 64) void k_gemv_dot4(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
     const float *__restrict__ sx, const int32_t *__restrict__ xsum, int M, int64_t N, int KC,
-    float *__restrict__ Y, int32_t *__restrict__ ACC)
+    float *__restrict__ Y, int32_t *__restrict__ ACC, int rs)
 {
     __shared__ int red[kDot4Waves][MT][64];
     const int lane = threadIdx.x & 63;
@@ -76,7 +76,6 @@ __global__ __launch_bounds__(kDot4Waves * 64) void k_gemv_dot4(
         red[wave][m][lane] = a1[m] + (a4[m] >> 2) + (a16[m] >> 4);
     __syncthreads();
 
-    const float gamma = w_scale[0];
     for (int o = threadIdx.x; o < MT * 64; o += kDot4Waves * 64) {
         const int m = o >> 6;
         const int r = o & 63;
@@ -91,13 +90,13 @@ __global__ __launch_bounds__(kDot4Waves * 64) void k_gemv_dot4(
         if (ACC)
             ACC[(int64_t)m * N + n] = acc;
         if (Y)
-            Y[(int64_t)m * N + n] = (float)acc * (gamma * sx[m]);
+            Y[(int64_t)m * N + n] = (float)acc * (w_scale[rs ? n : 0] * sx[m]);
     }
 }
 
 }  // namespace
 
-hipError_t launch_gemv_dot4(const uint4 *Wp, const float *w_scale, const int8_t *Xq, int64_t ldq,
+hipError_t launch_gemv_dot4(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq,
                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
                             int32_t *acc, hipStream_t s)
 {
@@ -106,16 +105,16 @@ hipError_t launch_gemv_dot4(const uint4 *Wp, const float *w_scale, const int8_t 
     const dim3 grid((unsigned)NB), block(kDot4Waves * 64);
     switch (M) {
     case 1:
-        hipLaunchKernelGGL(k_gemv_dot4<1>, grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, Y, acc);
+        hipLaunchKernelGGL(k_gemv_dot4<1>, grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, Y, acc, (int)row_scales);
         break;
     case 2:
-        hipLaunchKernelGGL(k_gemv_dot4<2>, grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, Y, acc);
+        hipLaunchKernelGGL(k_gemv_dot4<2>, grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, Y, acc, (int)row_scales);
         break;
     case 3:
-        hipLaunchKernelGGL(k_gemv_dot4<3>, grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, Y, acc);
+        hipLaunchKernelGGL(k_gemv_dot4<3>, grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, Y, acc, (int)row_scales);
         break;
     default:
-        hipLaunchKernelGGL(k_gemv_dot4<4>, grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, Y, acc);
+        hipLaunchKernelGGL(k_gemv_dot4<4>, grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, Y, acc, (int)row_scales);
         break;
     }
     return hipGetLastError();

@@ -62,6 +62,44 @@ __global__ __launch_bounds__(256) void k_gamma(const double *__restrict__ rowsum
         gamma[0] = (N > 0 && K > 0) ? (float)(total / (double)(N * K)) : 0.0f;
 }
 
+// Row-group scales: workgroup g adds the row sums of group g (rows end[g-1] .. end[g]-1)
+// in row order exactly as k_gamma does for the whole matrix, then writes the group's
+// scale to each of its rows.
+__global__ __launch_bounds__(256) void k_gamma_groups(const double *__restrict__ rowsum, int64_t K, RowGroups groups,
+                                                      float *__restrict__ row_scale)
+{
+    __shared__ double buf[256];
+    __shared__ float s_gamma;
+    const int gi = blockIdx.x;
+    const int64_t r0 = gi == 0 ? 0 : groups.end[gi - 1], r1 = groups.end[gi];
+    double total = 0.0;
+    for (int64_t n0 = r0; n0 < r1; n0 += 256) {
+        const int64_t n = n0 + threadIdx.x;
+        buf[threadIdx.x] = (n < r1 && K > 0) ? rowsum[n] : 0.0;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int cnt = (int)((r1 - n0) < 256 ? (r1 - n0) : 256);
+            for (int i = 0; i < cnt; ++i)
+                total += buf[i];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        s_gamma = K > 0 ? (float)(total / (double)((r1 - r0) * K)) : 0.0f;
+    __syncthreads();
+    for (int64_t n = r0 + threadIdx.x; n < r1; n += 256)
+        row_scale[n] = s_gamma;
+}
+
+// One group per row: the row's own mean |W|.
+__global__ __launch_bounds__(256) void k_gamma_per_row(const double *__restrict__ rowsum, int64_t N, int64_t K,
+                                                       float *__restrict__ row_scale)
+{
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n < N)
+        row_scale[n] = K > 0 ? (float)(rowsum[n] / (double)K) : 0.0f;
+}
+
 __device__ inline uint32_t code_of(float w, float half)
 {
     // t + 1 with t = +1 if w > gamma/2, -1 if w < -gamma/2, 0 otherwise.
@@ -69,8 +107,9 @@ __device__ inline uint32_t code_of(float w, float half)
 }
 
 // One thread per packed row segment (16 bytes = 64 codes of one row in one chunk).
+// gstride 0: one scale for the matrix (gamma[0]); 1: row n's scale is gamma[n].
 __global__ __launch_bounds__(256) void k_pack(const float *__restrict__ W, int64_t N, int64_t K, int64_t KC,
-                                              int64_t total, const float *__restrict__ gamma,
+                                              int64_t total, const float *__restrict__ gamma, int gstride,
                                               uint4 *__restrict__ Wp)
 {
     const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -81,7 +120,7 @@ __global__ __launch_bounds__(256) void k_pack(const float *__restrict__ W, int64
     const int64_t c = chunk % KC;
     const int64_t rb = chunk / KC;
     const int64_t n = rb * 64 + r;
-    const float half = gamma[0] * 0.5f;
+    const float half = gamma[n < N ? n * gstride : 0] * 0.5f;
     uint32_t words[4];
     const bool full = (n < N) && (c * 64 + 64 <= K) && ((K & 3) == 0);
 #pragma unroll
@@ -153,7 +192,29 @@ hipError_t launch_pack(const float *W, int64_t N, int64_t K, uint4 *Wp, float *g
     const int64_t total = NB * KC * 64;
     if (total > 0)
         hipLaunchKernelGGL(k_pack, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, W, N, K, KC, total,
-                           gamma, Wp);
+                           gamma, 0, Wp);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_rows(const float *W, int64_t N, int64_t K, const RowGroups *groups, uint4 *Wp,
+                            float *row_scale, double *rowsum, hipStream_t s)
+{
+    const int64_t NB = (N + 63) / 64;
+    const int64_t KC = (K + 63) / 64;
+    if (N == 0)
+        return hipSuccess;
+    if (K > 0)
+        hipLaunchKernelGGL(k_row_abs_sum, dim3((unsigned)NB), dim3(64), 0, s, W, N, K, rowsum);
+    if (groups)
+        hipLaunchKernelGGL(k_gamma_groups, dim3((unsigned)groups->n), dim3(256), 0, s, rowsum, K, *groups,
+                           row_scale);
+    else
+        hipLaunchKernelGGL(k_gamma_per_row, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, rowsum, N, K,
+                           row_scale);
+    const int64_t total = NB * KC * 64;
+    if (total > 0)
+        hipLaunchKernelGGL(k_pack, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, W, N, K, KC, total,
+                           row_scale, 1, Wp);
     return hipGetLastError();
 }
 

@@ -104,6 +104,24 @@ __device__ inline float load_scale_vmem(const float *p)
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 0, 0, 0));
 }
 
+// The weight scales of output rows n .. n+3: with row scales, entries n .. n+3 of the
+// N-entry scale array (an entry past N reads 0); otherwise the matrix's one scale, four
+// times. Four dword loads in both cases, with no branch: a branch here would make the
+// compiler wait for the loads where the two paths meet instead of where the values are
+// used, and offsets that are not constant apart keep it from merging the four loads into
+// one 16-byte load whose range check would cover all four entries at once. N <= 2^30.
+__device__ inline float4 load_scales4(const float *w_scale, int64_t n, int64_t N, bool rows)
+{
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(w_scale), (short)0, rows ? (int)(uint32_t)min(4 * N, (int64_t)0xFFFFFFFF) : 4,
+        0x00020000);
+    const uint32_t off = rows ? (uint32_t)(4 * n) : 0u, step = rows ? 4u : 0u;
+    return make_float4(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off + step, 0, 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off + 2 * step, 0, 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off + 3 * step, 0, 0)));
+}
+
 __device__ inline int sum_bytes_s8(uint32_t p)
 {
     return (int)(int8_t)(p & 0xff) + (int)(int8_t)((p >> 8) & 0xff) + (int)(int8_t)((p >> 16) & 0xff) +

@@ -31,6 +31,23 @@ SHAPES_100B = (("qkv", 10240, 8192), ("o", 8192, 8192), ("gate_up", 57344, 8192)
 # Workload ids used for seeding.
 CFG_TINY, CFG_2B_DECODE, CFG_7B_DECODE, CFG_2B_PREFILL, CFG_100B_DECODE = 1, 2, 3, 4, 5
 
+# Row groups of the fused matrices (the model's separate matrices stacked in output-row
+# order): Q, K, V (grouped-query attention: K and V narrower at 2B and 100B) and gate, up.
+# Every other matrix is one group.
+_FUSED_GROUPS = {
+    "2b": {"qkv": (2560, 640, 640), "gate_up": (6912, 6912)},
+    "7b": {"qkv": (4096, 4096, 4096), "gate_up": (11008, 11008)},
+    "100b": {"qkv": (8192, 1024, 1024), "gate_up": (28672, 28672)},
+}
+_CFG_MODEL = {CFG_2B_DECODE: "2b", CFG_2B_PREFILL: "2b", CFG_7B_DECODE: "7b", CFG_100B_DECODE: "100b"}
+
+
+def row_groups(cfg: int, name: str, N: int) -> tuple:
+    """Row counts of the groups of matrix ``name`` (N rows) in workload ``cfg``."""
+    groups = _FUSED_GROUPS.get(_CFG_MODEL.get(cfg, ""), {}).get(name, (N,))
+    assert sum(groups) == N, (cfg, name, N, groups)
+    return groups
+
 
 def gaussian(shape, seed: int, std=None) -> np.ndarray:
     """fp32 N(0,1) draws from PCG64(seed), optionally times a fp32 std."""

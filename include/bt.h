@@ -25,8 +25,12 @@
  *    (but the kernels still stay in bounds).
  *  - Calls on different streams may run concurrently; a call reads only its
  *    inputs and writes only its outputs. The library holds no mutable global state
- *    other than a thread-local error string and a once-per-process kernel attribute
- *    (the prefill kernel's LDS cap).
+ *    other than a thread-local error string.
+ *  - Row-group weight scales (the "_rows" / "_rs" entry points): the rows of W may be
+ *    cut into groups that each get the absmean scale of their own rows (the Q, K and
+ *    V blocks of a fused projection, or one group per row). The scale then travels as
+ *    an array of N fp32 values, one per output row, and Y[m,n] uses entry n. Integer
+ *    results are computed exactly as with one scale per matrix.
  */
 #ifndef BT_H
 #define BT_H
@@ -51,6 +55,8 @@ typedef int32_t bt_status;
 #define BT_MAX_K 131072
 /* Largest token count the decode GEMV entry point accepts. */
 #define BT_GEMV_MAX_M 16
+/* Largest number of explicit row groups bt_pack_weights_rows takes. */
+#define BT_MAX_ROW_GROUPS 8
 
 /* Decode GEMV kernel choices for bt_ternary_gemv_algo. */
 #define BT_GEMV_AUTO 0 /* pick by M from the library's launch table             */
@@ -95,6 +101,27 @@ size_t bt_pack_workspace_bytes(int64_t N, int64_t K);
  */
 bt_status bt_pack_weights(const float *W, int64_t N, int64_t K, void *Wp, float *w_scale,
                           void *workspace, void *stream);
+
+/*
+ * bt_pack_weights_rows -- bt_pack_weights with row-group scales. Follows the BitNet GPU
+ * guide, "Frequently Asked Questions" (the kernel wrapper assumes model-specific
+ * quantization scales and group dimensions): here a group is a run of output rows that
+ * was one matrix of the model (fused Q/K/V, fused gate/up), or a single row.
+ *   group_rows  HOST array of ngroups row counts (each >= 1, summing to N), in row
+ *               order, 1 <= ngroups <= BT_MAX_ROW_GROUPS; or NULL for one group per
+ *               row (ngroups ignored).
+ *   row_scale   output, N fp32 on the device: row n receives its group's scale,
+ *               computed like bt_pack_weights' gamma over the group's rows alone (each
+ *               row summed k = 0..K-1 in fp64, the group's row sums in row order in
+ *               fp64, one division, one rounding to fp32). Codes of row n use
+ *               row_scale[n] / 2 as the threshold.
+ *   W, Wp, workspace   as for bt_pack_weights (same layout and workspace size).
+ * With K == 0 every scale is 0. Errors: BT_ERR_SHAPE when the groups do not cover the
+ * N rows exactly or a group is empty; otherwise those of bt_pack_weights.
+ */
+bt_status bt_pack_weights_rows(const float *W, int64_t N, int64_t K, const int64_t *group_rows,
+                               int64_t ngroups, void *Wp, float *row_scale, void *workspace,
+                               void *stream);
 
 /*
  * bt_unpack_weights -- inverse of the packing (a test and inspection aid):
@@ -145,6 +172,13 @@ bt_status bt_ternary_gemv_algo(const void *Wp, const float *w_scale, const int8_
                                const float *x_scale, const int32_t *x_sum, int64_t M, int64_t N,
                                int64_t K, float *Y, int32_t *acc, int32_t algo, void *stream);
 
+/* bt_ternary_gemv_algo with row scales: row_scale[N] (from bt_pack_weights_rows) in
+ * place of w_scale, Y[m,n] = fp32(acc) * (row_scale[n] * s_x[m]). Same passages as
+ * bt_ternary_gemv, plus the GPU guide's FAQ on model-specific scales. */
+bt_status bt_ternary_gemv_rs(const void *Wp, const float *row_scale, const int8_t *Xq,
+                             const float *x_scale, const int32_t *x_sum, int64_t M, int64_t N,
+                             int64_t K, float *Y, int32_t *acc, int32_t algo, void *stream);
+
 /*
  * bt_ternary_gemm -- prefill product for any M >= 1 on int8 MFMA: the packed
  * weight tiles are unpacked in registers straight into MFMA operands, the int8
@@ -182,6 +216,15 @@ bt_status bt_ternary_gemm_ws(const void *Wp, const float *w_scale, const int8_t 
                              int64_t K, float *Y, int32_t *acc, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* bt_ternary_gemm_ws with row scales: row_scale[N] (from bt_pack_weights_rows) in place
+ * of w_scale, Y[m,n] = fp32(acc) * (row_scale[n] * s_x[m]); workspace as for
+ * bt_ternary_gemm_ws (NULL: no split). Same passages as bt_ternary_gemm, plus the GPU
+ * guide's FAQ on model-specific scales. */
+bt_status bt_ternary_gemm_rs(const void *Wp, const float *row_scale, const int8_t *Xq,
+                             const float *x_scale, const int32_t *x_sum, int64_t M, int64_t N,
+                             int64_t K, float *Y, int32_t *acc, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /*
  * bt_ternary_linear -- the whole per-call path of the layer in one entry point:
  * fp32 activations in, fp32 outputs out (per-token absmax int8 quantization, the
@@ -207,6 +250,13 @@ size_t bt_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 bt_status bt_ternary_linear(const void *Wp, const float *w_scale, const float *X, int64_t M,
                             int64_t N, int64_t K, float *Y, int32_t *acc, void *workspace,
                             void *stream);
+
+/* bt_ternary_linear with row scales: row_scale[N] (from bt_pack_weights_rows) in place of
+ * w_scale; the same routes, workspace (bt_linear_workspace_bytes) and errors. Same
+ * passages as bt_ternary_linear, plus the GPU guide's FAQ on model-specific scales. */
+bt_status bt_ternary_linear_rs(const void *Wp, const float *row_scale, const float *X, int64_t M,
+                               int64_t N, int64_t K, float *Y, int32_t *acc, void *workspace,
+                               void *stream);
 
 /* Static text for a status code. */
 const char *bt_status_str(bt_status s);
