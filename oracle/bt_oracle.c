@@ -35,7 +35,7 @@
  *      s_x = a / 127.0f; a zero row gives q = 0 and s_x = 0;
  *  R5  y = acc * gamma * s_x evaluated in fp64 and rounded once to fp32;
  *  R6  non-finite inputs are outside the contract: the oracle rejects them;
- *  R7  row-group scales (the "_rows" functions): the rows of W are cut, in order,
+ *  R12 row-group scales (the "_rows" functions): the rows of W are cut, in order,
  *      into groups that are separate matrices stored one above the other (the Q,
  *      K and V blocks of a fused projection; one row per group at the finest);
  *      each group gets the R2 scale of its own rows, its codes use that scale
@@ -166,7 +166,7 @@ int oracle_scale_epilogue(const int32_t *acc, float gamma, const float *s_x,
     return 0;
 }
 
-/* Row-group weight scales (R7): the rows are cut, in order, into nseg groups of
+/* Row-group weight scales (R12): the rows are cut, in order, into nseg groups of
  * seg_rows[s] >= 1 rows (seg_rows == NULL: each of the N rows is its own group);
  * row_scale[n] receives the mean |W| of row n's group alone, summed as in R2.
  * Follows the BitNet GPU guide, "Frequently Asked Questions" (the kernel wrapper
@@ -190,7 +190,7 @@ int oracle_absmean_rows(const float *W, int64_t N, int64_t K, const int64_t *seg
     return n0 == N ? 0 : 2;
 }
 
-/* Codes of every row against its own scale (R3 with gamma_n, R7). */
+/* Codes of every row against its own scale (R3 with gamma_n, R12). */
 int oracle_ternarize_rows(const float *W, int64_t N, int64_t K, const float *row_scale,
                           int8_t *T)
 {
@@ -200,7 +200,7 @@ int oracle_ternarize_rows(const float *W, int64_t N, int64_t K, const float *row
     return 0;
 }
 
-/* y[m,n] = acc[m,n] * gamma_n * s_x[m], in fp64, rounded once to fp32 (R5, R7).
+/* y[m,n] = acc[m,n] * gamma_n * s_x[m], in fp64, rounded once to fp32 (R5, R12).
  * Follows the "bit-floor" page, "The core math" (weight scale times activation
  * scale times the integer dot), with the weight scale of output row n. */
 int oracle_scale_epilogue_rows(const int32_t *acc, const float *row_scale, const float *s_x,
