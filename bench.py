@@ -53,7 +53,9 @@ CSRC = os.path.join(ROOT, "bit_ternary_weight_absmean_amd", "csrc")
 # Sources each dominant kernel is built from (their hash tags a traffic summary).
 KERNEL_SOURCES = {
     "k_linear_decode": ["decode.hip", "wave.h", "bt_internal.h"],
-    "k_gemv_direct": ["decode.hip", "bt_internal.h"],
+    "k_gemv_direct": ["decode.hip", "wave.h", "bt_internal.h"],
+    "k_gemv_dot4": ["gemv.hip", "bt_internal.h"],
+    "k_gemv_lut": ["lut.hip", "bt_internal.h"],
     "k_gemm": ["gemm.hip", "bt_internal.h"],
 }
 
@@ -67,6 +69,8 @@ def parse():
     p.add_argument("--m", type=int, default=None, help="tokens per call (default: 1 for decode, 2048 for prefill)")
     p.add_argument("--eager", action="store_true", help="launch kernels one by one instead of replaying graphs")
     p.add_argument("--split", action="store_true", help="time bt_quant_act + product as two launches per matrix")
+    p.add_argument("--gemv-algo", choices=("mfma", "dot4", "lut"), default="mfma",
+                   help="with --split at M <= 16: the decode product kernel (bt_ternary_gemv_algo)")
     p.add_argument("--row-scales", action="store_true",
                    help="row-group weight scales: fused Q/K/V and gate/up matrices packed with one scale per "
                         "block (bt_pack_weights_rows), products through the row-scale entry points")
@@ -190,12 +194,13 @@ def run_gpu(args, spec):
     elif spec["prefill"] or M > bt.GEMV_MAX_M:
         kernel = "k_gemm"
     else:
-        kernel = "k_gemv_direct"
+        kernel = {"mfma": "k_gemv_direct", "dot4": "k_gemv_dot4", "lut": "k_gemv_lut"}[args.gemv_algo]
+    algo = {"mfma": bt.GEMV_MFMA, "dot4": bt.GEMV_DOT4, "lut": bt.GEMV_LUT}[args.gemv_algo]
 
     def product(pw, q, out_y, j):
         if kernel == "k_gemm":
             return bt.ternary_gemm(pw, q, out_y=out_y, workspace=gws[j])
-        return bt.ternary_gemv(pw, q, out_y=out_y)
+        return bt.ternary_gemv(pw, q, out_y=out_y, algo=algo)
 
     def step():
         for row in packed:

@@ -13,6 +13,7 @@ from ._lib import BTError, lib
 from .api import (
     GEMV_AUTO,
     GEMV_DOT4,
+    GEMV_LUT,
     GEMV_MAX_M,
     GEMV_MFMA,
     PackedWeight,
@@ -32,7 +33,7 @@ from .api import (
 )
 
 __all__ = [
-    "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_MFMA", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
+    "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_LUT", "GEMV_MFMA", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
     "gemm_workspace", "gemm_workspace_bytes", "linear", "linear_workspace_bytes", "pack_weights", "pack_weights_rows", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
     "ternary_gemv", "unpack_weights",
 ]

@@ -200,7 +200,7 @@ static bt_status gemv_impl(const void *Wp, const float *w_scale, bool rows, cons
     if (M > BT_GEMV_MAX_M)
         return fail(BT_ERR_UNSUPPORTED, "gemv takes M <= %d (got %lld); use bt_ternary_gemm", BT_GEMV_MAX_M,
                     (long long)M);
-    if (algo != BT_GEMV_AUTO && algo != BT_GEMV_DOT4 && algo != BT_GEMV_MFMA)
+    if (algo != BT_GEMV_AUTO && algo != BT_GEMV_DOT4 && algo != BT_GEMV_MFMA && algo != BT_GEMV_LUT)
         return fail(BT_ERR_UNSUPPORTED, "unknown gemv algo %d", (int)algo);
     if (M == 0 || N == 0)
         return ok();
@@ -208,11 +208,26 @@ static bt_status gemv_impl(const void *Wp, const float *w_scale, bool rows, cons
         algo = BT_GEMV_MFMA;
     if (algo == BT_GEMV_DOT4 && M > 4)
         return fail(BT_ERR_UNSUPPORTED, "dot4 gemv takes M <= 4 (got %lld)", (long long)M);
-    const int64_t ldq = bt_act_row_bytes(K);
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (algo == BT_GEMV_LUT) {
+        if (M != 1)
+            return fail(BT_ERR_UNSUPPORTED, "lut gemv takes M == 1 (got %lld)", (long long)M);
+        int dev = 0, lds_max = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return fail(BT_ERR_HIP, "cannot query the LDS limit");
+        if (bt::gemv_lut_lds_bytes(K) + 1024 > (size_t)lds_max)
+            return fail(BT_ERR_UNSUPPORTED, "lut gemv tables for K = %lld need %zu bytes of LDS (limit %d)",
+                        (long long)K, bt::gemv_lut_lds_bytes(K), lds_max);
+        if (K == 0)
+            return gemv_impl(Wp, w_scale, rows, Xq, x_scale, x_sum, M, N, K, Y, acc, BT_GEMV_MFMA, stream);
+    }
+    const int64_t ldq = bt_act_row_bytes(K);
     const uint4 *W = static_cast<const uint4 *>(Wp);
     hipError_t e = (algo == BT_GEMV_DOT4)
                        ? bt::launch_gemv_dot4(W, w_scale, rows, Xq, ldq, x_scale, x_sum, M, N, K, Y, acc, s)
+                   : (algo == BT_GEMV_LUT)
+                       ? bt::launch_gemv_lut(W, w_scale, rows, Xq, x_scale, x_sum, N, K, Y, acc, s)
                        : bt::launch_gemv_mfma(W, w_scale, rows, Xq, ldq, x_scale, x_sum, M, N, K, Y, acc, s);
     return hip_status(e, "bt_ternary_gemv launch");
 }

@@ -63,6 +63,11 @@ hipError_t launch_gemv_dot4(const uint4 *Wp, const float *w_scale, bool row_scal
 hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq,
                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
                             int32_t *acc, hipStream_t s);
+// Table-lookup GEMV for one token; the LDS bytes its tables take.
+hipError_t launch_gemv_lut(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq,
+                           const float *sx, const int32_t *xsum, int64_t N, int64_t K, float *Y, int32_t *acc,
+                           hipStream_t s);
+size_t gemv_lut_lds_bytes(int64_t K);
 // Fused decode (quantize + product + epilogue) for M <= 4; LDS bytes it needs.
 hipError_t launch_linear_decode(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M,
                                 int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s);

@@ -525,3 +525,48 @@ def test_linear_100b_gate_up_m1_sampled():
     Y, acc = bt.linear(to_dev(X), pw, want_acc=True)
     np.testing.assert_array_equal(acc.cpu().numpy()[:, rows], acc_ref)
     assert tol_ok(Y.cpu().numpy()[:, rows], oracle.scale_epilogue(acc_ref, g, s))
+
+
+# ------------------------------------------------------- table-lookup GEMV (M = 1)
+def _lut_fits(K):
+    props = torch.cuda.get_device_properties(0)
+    limit = getattr(props, "shared_memory_per_block", 65536)
+    return ((K + 63) // 64) * 1024 + 1024 <= limit
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (100, 300), (65, 129), (17, 64), (3840, 2560), (2560, 2560),
+                                 (13824, 2560), (2560, 6912), (12288, 4096)])
+def test_gemv_lut(N, K):
+    """BT_GEMV_LUT (tables of code-pair sums in LDS) against the oracle and bit-identical to MFMA."""
+    note(f"gemv lut N={N} K={K}")
+    if not _lut_fits(K):
+        pytest.skip(f"LUT tables for K = {K} exceed this device's per-workgroup LDS")
+    W = synth.gaussian((N, K), 9900 + N + K, 0.02)
+    X = synth.gaussian((1, K), 9950 + K)
+    ref = oracle_layer(W, X)
+    pw = gpu_pack(W)
+    q = gpu_quant(X)
+    check_product(pw, q, ref, 1, N, bt.ternary_gemv, algo=bt.GEMV_LUT)
+    Y2, acc2 = bt.ternary_gemv(pw, q, want_acc=True, algo=bt.GEMV_MFMA)
+    Y1, acc1 = bt.ternary_gemv(pw, q, want_acc=True, algo=bt.GEMV_LUT)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc1.cpu().numpy(), acc2.cpu().numpy())
+    np.testing.assert_array_equal(Y1.cpu().numpy(), Y2.cpu().numpy())
+
+
+def test_gemv_lut_row_scales_and_limits():
+    note("gemv lut row scales / limits")
+    N, K, groups = 768, 700, [640, 64, 64]
+    W = synth.gaussian((N, K), 9960, 0.02)
+    W[640:704] *= np.float32(9.0)
+    X = synth.gaussian((1, K), 9961)
+    ref = oracle.linear_rows(W, X, groups)
+    pw = bt.pack_weights_rows(to_dev(W), groups)
+    Y, acc = bt.ternary_gemv(pw, bt.quant_act(to_dev(X)), want_acc=True, algo=bt.GEMV_LUT)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    assert tol_ok(Y.cpu().numpy(), ref["Y"])
+    # two tokens: the LUT kernel takes one
+    X2 = synth.gaussian((2, K), 9962)
+    with pytest.raises(bt.BTError):
+        bt.ternary_gemv(gpu_pack(W), gpu_quant(X2), algo=bt.GEMV_LUT)
