@@ -47,9 +47,12 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_absmean_rows.argtypes = [vp, i64, i64, vp, i64, vp]
     lib.oracle_ternarize_rows.argtypes = [vp, i64, i64, vp, vp]
     lib.oracle_scale_epilogue_rows.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.oracle_absmax_rows.argtypes = [vp, i64, i64, vp]
+    lib.oracle_binarize.argtypes = [vp, i64, i64, vp]
     for f in ("oracle_absmean", "oracle_ternarize", "oracle_quant_act",
               "oracle_ternary_matmul", "oracle_scale_epilogue", "oracle_absmean_rows",
-              "oracle_ternarize_rows", "oracle_scale_epilogue_rows"):
+              "oracle_ternarize_rows", "oracle_scale_epilogue_rows", "oracle_absmax_rows",
+              "oracle_binarize"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -219,3 +222,50 @@ def linear_rows(W, X, seg_rows=None, lib=None) -> dict:
     acc = ternary_matmul(T, Q, lib)
     Y = scale_epilogue_rows(acc, row_scale, s_x, lib)
     return {"row_scale": row_scale, "T": T, "Q": Q, "s_x": s_x, "qsum": qsum, "acc": acc, "Y": Y}
+
+
+def absmax_rows(V, lib=None) -> np.ndarray:
+    """max |V[r, :]| per row (fp32 [R]); a matrix's absmax is absmax_rows(V.reshape(1, -1)).
+
+    "bit-floor" page, "What's inside" (pack.rs / scale.rs: absmax scales).
+    """
+    lib = lib or load()
+    V = _f32(V)
+    R, C = V.shape
+    out = np.empty(R, dtype=np.float32)
+    _check(lib.oracle_absmax_rows(_ptr(V), R, C, _ptr(out)))
+    return out
+
+
+def binarize(V, lib=None) -> np.ndarray:
+    """+1 where V >= 0, -1 elsewhere (int8), the 1-bit operands of "The core math"."""
+    lib = lib or load()
+    V = _f32(V)
+    R, C = V.shape
+    B = np.empty((R, C), dtype=np.int8)
+    _check(lib.oracle_binarize(_ptr(V), R, C, _ptr(B)))
+    return B
+
+
+def binary_layer(W, X, lib=None) -> dict:
+    """W1A1: y = max|W| * max|x_m| * sum_k sign(W) sign(x) ("bit-floor" page, "The core math")."""
+    lib = lib or load()
+    s_w = absmax_rows(np.asarray(W, np.float32).reshape(1, -1), lib)[0]
+    Wb = binarize(W, lib)
+    Xb = binarize(X, lib)
+    s_x = absmax_rows(X, lib)
+    acc = ternary_matmul(Wb, Xb, lib)
+    Y = scale_epilogue(acc, s_w, s_x, lib)
+    return {"s_w": s_w, "Wb": Wb, "Xb": Xb, "s_x": s_x, "acc": acc, "Y": Y}
+
+
+def ternary_a1_layer(W, X, lib=None) -> dict:
+    """W1.58A1: ternary weights (absmean, as in ``linear``) against binarized tokens."""
+    lib = lib or load()
+    gamma = absmean(W, lib)
+    T = ternarize(W, gamma, lib)
+    Xb = binarize(X, lib)
+    s_x = absmax_rows(X, lib)
+    acc = ternary_matmul(T, Xb, lib)
+    Y = scale_epilogue(acc, gamma, s_x, lib)
+    return {"gamma": gamma, "T": T, "Xb": Xb, "s_x": s_x, "acc": acc, "Y": Y}

@@ -40,6 +40,11 @@
  *      K and V blocks of a fused projection; one row per group at the finest);
  *      each group gets the R2 scale of its own rows, its codes use that scale
  *      (R3), and y uses the scale of its output row (R5 with gamma_n).
+ *  R13 1-bit operands (the binary W1A1 and the ternary-weight W1.58A1 products):
+ *      a value binarizes to +1 when v >= 0 and to -1 when v < 0; the scale of a
+ *      binarized weight matrix is its absmax, that of a binarized token its
+ *      absmax; y = acc * scale_w * scale_x as in R5 (scale_w = gamma for
+ *      ternary weights).
  *
  * Every entry point returns 0 on success and 1 when an input is not finite
  * (2 when the row groups do not cover the N rows exactly).
@@ -209,5 +214,37 @@ int oracle_scale_epilogue_rows(const int32_t *acc, const float *row_scale, const
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
             Y[m * N + n] = (float)((double)acc[m * N + n] * (double)row_scale[n] * (double)s_x[m]);
+    return 0;
+}
+
+/* max |V[r, :]| of every row of V [R,C] (R13; an empty row gives 0). A matrix's absmax
+ * is this with R = 1 over all its entries. Follows the "bit-floor" page, "What's
+ * inside" (pack.rs: absmax scale for binary weights; scale.rs: absmax scales). */
+int oracle_absmax_rows(const float *V, int64_t R, int64_t C, float *amax)
+{
+    for (int64_t r = 0; r < R; ++r) {
+        float a = 0.0f;
+        for (int64_t c = 0; c < C; ++c) {
+            const float v = V[r * C + c];
+            if (!isfinite(v))
+                return 1;
+            if (fabsf(v) > a)
+                a = fabsf(v);
+        }
+        amax[r] = a;
+    }
+    return 0;
+}
+
+/* B = +1 where V >= 0, -1 where V < 0 (R13): one bit per value. Follows the
+ * "bit-floor" page, "The core math" (binary weights are +1 or -1) and "What's
+ * inside" (scale.rs: activations quantized to packed bits before each GEMV). */
+int oracle_binarize(const float *V, int64_t R, int64_t C, int8_t *B)
+{
+    for (int64_t i = 0; i < R * C; ++i) {
+        if (!isfinite(V[i]))
+            return 1;
+        B[i] = V[i] >= 0.0f ? 1 : -1;
+    }
     return 0;
 }

@@ -36,6 +36,10 @@ MUTANTS = {
     "rows_codes_first_scale": ("row_scale[n], T + n * K", "row_scale[0], T + n * K"),
     "rows_group_start_stuck": ("        n0 += rows;\n    }\n    return n0 == N", "        n0 += 0;\n    }\n    return n0 == N"),
     "rows_epilogue_drops_scale": ("(double)acc[m * N + n] * (double)row_scale[n]", "(double)acc[m * N + n]"),
+    "binarize_zero_negative": ("B[i] = V[i] >= 0.0f ? 1 : -1;", "B[i] = V[i] > 0.0f ? 1 : -1;"),
+    "binarize_flipped": ("B[i] = V[i] >= 0.0f ? 1 : -1;", "B[i] = V[i] >= 0.0f ? -1 : 1;"),
+    "absmax_keeps_min": ("if (fabsf(v) > a)", "if (fabsf(v) < a)"),
+    "absmax_without_abs": ("if (fabsf(v) > a)\n                a = fabsf(v);", "if (v > a)\n                a = v;"),
 }
 
 
@@ -57,7 +61,10 @@ def _battery(lib):
                  "test_negating_w_negates_y", "test_y_equals_matmul_of_dequantized_operands",
                  "test_bitplane_popcount_form", "test_row_group_scales_are_exact_group_means",
                  "test_row_group_codes_gaussian_zero_fraction", "test_row_scales_power_of_two_rows",
-                 "test_one_group_is_the_per_matrix_layer", "test_row_groups_equal_separate_matrices"):
+                 "test_one_group_is_the_per_matrix_layer", "test_row_groups_equal_separate_matrices",
+                 "test_binary_acc_is_the_pages_xnor_popcount", "test_ternary_a1_acc_is_the_pages_bitplane_form",
+                 "test_binarize_signs_and_zero", "test_absmax_rows_is_numpy_max_abs",
+                 "test_binary_layer_exact_when_magnitudes_are_constant"):
         run(name, getattr(pins, name))
     return failed
 

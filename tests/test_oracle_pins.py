@@ -437,3 +437,69 @@ def test_row_groups_must_cover_the_rows(orc):
     for bad in ([4, 5], [4, 7], [0, 10], [10, 0]):
         with pytest.raises(oracle.OracleInputError):
             oracle.absmean_rows(W, bad, orc)
+
+
+# ------------------------------------------------ 1-bit operands (W1A1, W1.58A1)
+def _bits(B):
+    """Row r of a +-1 (or ternary) int8 matrix as Python ints: bit k set where B[r, k] < 0."""
+    return [sum(1 << k for k in range(B.shape[1]) if B[r, k] < 0) for r in range(B.shape[0])]
+
+
+def _popcount(v):
+    return bin(v).count("1")
+
+
+def test_binary_acc_is_the_pages_xnor_popcount(orc):
+    """acc of the W1A1 oracle equals 2 * POPCNT(XNOR(W, X)) - K, the binary GEMV of the
+    "bit-floor" page's core math, evaluated on K-bit masks of the sign bits."""
+    lib = orc
+    for seed, (N, M, K) in enumerate([(5, 3, 1), (7, 2, 64), (9, 4, 65), (4, 2, 200)]):
+        W = synth.gaussian((N, K), 500 + seed, 0.02)
+        X = synth.gaussian((M, K), 510 + seed)
+        r = oracle.binary_layer(W, X, lib)
+        wb, xb, full = _bits(r["Wb"]), _bits(r["Xb"]), (1 << K) - 1
+        for m in range(M):
+            for n in range(N):
+                xnor = ~(wb[n] ^ xb[m]) & full
+                assert r["acc"][m, n] == 2 * _popcount(xnor) - K
+
+
+def test_ternary_a1_acc_is_the_pages_bitplane_form(orc):
+    """acc of the W1.58A1 oracle equals POPCNT(mag & XNOR(sign, x)) - POPCNT(mag & XOR(sign, x))
+    with mag = (t != 0), sign = (t < 0) and x = (x < 0), the page's ternary GEMV."""
+    lib = orc
+    for seed, (N, M, K) in enumerate([(6, 2, 3), (8, 3, 64), (5, 2, 130)]):
+        W = synth.gaussian((N, K), 520 + seed, 0.02)
+        X = synth.gaussian((M, K), 530 + seed)
+        r = oracle.ternary_a1_layer(W, X, lib)
+        T = r["T"]
+        mag = [sum(1 << k for k in range(K) if T[n, k] != 0) for n in range(N)]
+        sgn, xb, full = _bits(T), _bits(r["Xb"]), (1 << K) - 1
+        for m in range(M):
+            for n in range(N):
+                agree = mag[n] & ~(sgn[n] ^ xb[m]) & full
+                differ = mag[n] & (sgn[n] ^ xb[m])
+                assert r["acc"][m, n] == _popcount(agree) - _popcount(differ)
+
+
+def test_binarize_signs_and_zero(orc):
+    """v >= 0 gives +1 (so +0 and -0 give +1), v < 0 gives -1, down to the smallest subnormal."""
+    V = np.array([[-1e-45, 0.0, -0.0, 2.0, -3.5, 1e-45]], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.binarize(V, orc), [[-1, 1, 1, 1, -1, 1]])
+
+
+def test_absmax_rows_is_numpy_max_abs(orc):
+    V = synth.gaussian((7, 300), 540)
+    np.testing.assert_array_equal(oracle.absmax_rows(V, orc), np.max(np.abs(V), axis=1))
+    assert oracle.absmax_rows(V.reshape(1, -1), orc)[0] == np.max(np.abs(V))
+    assert oracle.absmax_rows(np.zeros((2, 0), np.float32), orc).tolist() == [0.0, 0.0]
+
+
+def test_binary_layer_exact_when_magnitudes_are_constant(orc):
+    """|W| = c and |x_m| = d_m (powers of two): binarizing loses nothing, so y = X W^T exactly."""
+    rng = np.random.default_rng(5)
+    K = 96
+    W = (np.float32(0.25) * np.where(rng.random((10, K)) < 0.5, -1, 1)).astype(np.float32)
+    X = (np.exp2(np.arange(3))[:, None] * np.where(rng.random((3, K)) < 0.5, -1, 1)).astype(np.float32)
+    r = oracle.binary_layer(W, X, orc)
+    np.testing.assert_array_equal(r["Y"], (X.astype(np.float64) @ W.astype(np.float64).T).astype(np.float32))
