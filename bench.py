@@ -24,6 +24,9 @@ Workloads (``--workload``):
   100b_decode 100B-class single-layer sweep at --m (1, 16): 3 independently seeded copies
               of {10240x8192, 8192x8192, 57344x8192, 8192x28672} (642 MB) -> GB/s.
   2b_prefill  2B-class prefill at --m (256, 2048): the 2B layer shapes, 30 layers -> TOPS.
+  onebit_decode  1-bit activations (bit-floor page's GEMV shapes): 4096x4096 binary weights
+              (bt_binary_gemv) and 4096x4096, 11008x4096 ternary weights
+              (bt_ternary_gemv_a1), 30 copies resident, at --m (default 1) -> GB/s.
 
 The dominant kernel's average duration comes from a second graph holding only the
 product launches of one step (for the fused decode route that is the whole step),
@@ -65,7 +68,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="2b_decode", choices=["2b_decode", "7b_decode", "100b_decode", "2b_prefill"])
+    p.add_argument("--workload", default="2b_decode", choices=["2b_decode", "7b_decode", "100b_decode", "2b_prefill",
+                                                                   "onebit_decode"])
     p.add_argument("--m", type=int, default=None, help="tokens per call (default: 1 for decode, 2048 for prefill)")
     p.add_argument("--eager", action="store_true", help="launch kernels one by one instead of replaying graphs")
     p.add_argument("--split", action="store_true", help="time bt_quant_act + product as two launches per matrix")
@@ -266,6 +270,144 @@ def run_gpu(args, spec):
     return dict(ms_step=ms_step, ms_prod=ms_prod, step_bytes=step_bytes, step_ops=step_ops,
                 prod_bytes=prod_bytes, n_prod=n_prod, resident=resident, setup_s=setup_s,
                 launch="eager" if args.eager else "hipGraph", fused=fused, kernel=kernel)
+
+
+# ------------------------------------------------- 1-bit activations (W1A1, W1.58A1)
+ONEBIT_COPIES = 30  # 30 x 17.3 MB of packed weights resident: twice the Infinity Cache
+
+
+def onebit_gemv_bytes(kind, M, N, K):
+    """Algorithmic bytes of one 1-bit-activation GEMV: packed weights (1 or 2 bits), the
+    activation bits, fp32 y written, the scales read."""
+    return N * K // (8 if kind == "binary" else 4) + M * K // 8 + 4 * M * N + 4 + 4 * M
+
+
+def run_onebit(args):
+    """The bit-floor page's GEMV shapes against binarized tokens: per copy, one
+    bt_binarize_act per layout and the three GEMVs (bt_binary_gemv for the binary matrix,
+    bt_ternary_gemv_a1 for the two ternary ones), replayed as one HIP graph."""
+    import torch
+
+    import bit_ternary_weight_absmean_amd as bt
+    from bit_ternary_weight_absmean_amd import synth
+
+    dev = torch.device("cuda:0")
+    M = args.m or 1
+    shapes = synth.SHAPES_ONEBIT
+    K = shapes[0][2]
+    ws = torch.empty(max(bt.pack_workspace_bytes(max(n for _, n, _ in shapes), K), 8), dtype=torch.uint8,
+                     device=dev)
+    packed = []
+    for c in range(ONEBIT_COPIES):
+        row = []
+        for j, (kind, N, _) in enumerate(shapes):
+            W = synth.device_gaussian((N, K), synth.weight_seed(synth.CFG_ONEBIT, c, j), dev, std=synth.WEIGHT_STD)
+            row.append(bt.pack_weights_binary(W, ws) if kind == "binary" else bt.pack_weights(W, ws))
+            del W
+        packed.append(row)
+    X = torch.from_numpy(synth.layer_activation(synth.CFG_ONEBIT, 0, M, K)).to(dev)
+    bp = bt.binarize_act(X, bt.BITS_PLAIN)
+    bc = bt.binarize_act(X, bt.BITS_CODES)
+    ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _, N, _ in shapes]
+    torch.cuda.synchronize()
+
+    def products():
+        for row in packed:
+            bt.binary_gemv(row[0], bp, out_y=ys[0])
+            bt.ternary_gemv_a1(row[1], bc, out_y=ys[1])
+            bt.ternary_gemv_a1(row[2], bc, out_y=ys[2])
+
+    def step():
+        for row in packed:
+            bt.binarize_act(X, bt.BITS_PLAIN, out=bp)
+            bt.binary_gemv(row[0], bp, out_y=ys[0])
+            bt.binarize_act(X, bt.BITS_CODES, out=bc)
+            bt.ternary_gemv_a1(row[1], bc, out_y=ys[1])
+            bt.ternary_gemv_a1(row[2], bc, out_y=ys[2])
+
+    stream = torch.cuda.Stream(device=dev)
+
+    def timed(fn):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            fn()
+        stream.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        stream.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        end.record(stream)
+        end.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    with torch.cuda.stream(stream):
+        step()
+        stream.synchronize()
+        ms_step = timed(step)
+        ms_prod = timed(products)
+    prod_bytes = ONEBIT_COPIES * sum(onebit_gemv_bytes(kind, M, N, K) for kind, N, _ in shapes)
+    step_bytes = prod_bytes + ONEBIT_COPIES * 2 * (4 * M * K + M * K // 8 + 4 * M)
+    ops = ONEBIT_COPIES * sum(2 * M * N * K for _, N, _ in shapes)
+    n_prod = ONEBIT_COPIES * len(shapes)
+    prod_us = ms_prod * 1e3 / n_prod
+    ach = prod_bytes / n_prod / (prod_us * 1e-6) / 1e9
+    cpu = None if args.no_cpu_baseline else run_onebit_cpu_baseline(args, M)
+    line = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": f"bit-floor GEMV shapes against binarized tokens (M={M}): 4096x4096 binary "
+                               f"(bt_binary_gemv), 4096x4096 and 11008x4096 ternary (bt_ternary_gemv_a1); "
+                               f"{ONEBIT_COPIES} copies resident", "M": M,
+                   "launch": "hipGraph",
+                   "step": "per copy: bt_binarize_act x 2 layouts + the three GEMVs"},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "detail": {"dominant_kernel": "k_gemv_bits", "kernel_avg_us": round(prod_us, 3),
+                   "algorithmic_bytes_per_launch": round(prod_bytes / n_prod),
+                   "gemv_GOPS": round(ops / (ms_prod * 1e-3) / 1e9, 1),
+                   "resident_packed_bytes": sum(p.data.numel() for row in packed for p in row)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_onebit_cpu_baseline(args, M):
+    """The oracle's W1A1 and W1.58A1 layers on copy 0's three matrices, single-threaded,
+    repeated for about --cpu-seconds."""
+    import oracle
+    from bit_ternary_weight_absmean_amd import synth
+
+    lib = oracle.load()
+    K = synth.SHAPES_ONEBIT[0][2]
+    X = synth.layer_activation(synth.CFG_ONEBIT, 0, M, K)
+    mats = [(kind, synth.layer_weight(synth.CFG_ONEBIT, 0, j, N, K)) for j, (kind, N, _) in
+            enumerate(synth.SHAPES_ONEBIT)]
+    done = passes = 0
+    t0 = time.perf_counter()
+    while True:
+        for kind, W in mats:
+            (oracle.binary_layer if kind == "binary" else oracle.ternary_a1_layer)(W, X, lib)
+            done += onebit_gemv_bytes(kind, M, W.shape[0], K)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds:
+            break
+    return {"value": round(done / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"copy 0's three matrices at M={M} (weights packed in the timed loop), {passes} passes"}
 
 
 # ----------------------------------------------------------- CPU baseline leg
@@ -477,6 +619,8 @@ def main():
         return 0
     global ROW_SCALES
     ROW_SCALES = args.row_scales
+    if args.workload == "onebit_decode":
+        return run_onebit(args)
     spec = workload_spec(args.workload, args.m)
     if ROW_SCALES:
         spec["desc"] += ", row-group weight scales (one per Q, K, V and gate, up block)"

@@ -11,6 +11,8 @@ from __future__ import annotations
 
 from ._lib import BTError, lib
 from .api import (
+    BITS_CODES,
+    BITS_PLAIN,
     GEMV_AUTO,
     GEMV_DOT4,
     GEMV_LUT,
@@ -18,21 +20,26 @@ from .api import (
     GEMV_MFMA,
     PackedWeight,
     act_row_bytes,
+    binarize_act,
+    binary_gemv,
     gemm_workspace,
     gemm_workspace_bytes,
     linear,
     linear_workspace_bytes,
     pack_weights,
+    pack_weights_binary,
     pack_weights_rows,
     pack_workspace_bytes,
     packed_weight_bytes,
     quant_act,
     ternary_gemm,
     ternary_gemv,
+    ternary_gemv_a1,
     unpack_weights,
 )
 
 __all__ = [
+    "BITS_CODES", "BITS_PLAIN", "binarize_act", "binary_gemv", "pack_weights_binary", "ternary_gemv_a1",
     "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_LUT", "GEMV_MFMA", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
     "gemm_workspace", "gemm_workspace_bytes", "linear", "linear_workspace_bytes", "pack_weights", "pack_weights_rows", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
     "ternary_gemv", "unpack_weights",

@@ -192,3 +192,59 @@ def linear(X: torch.Tensor, pw: PackedWeight, want_y=True, want_acc=False, out_y
     check(fn(_ptr(pw.data), _ptr(pw.scale), _ptr(X), M, pw.N, K, _ptr(Y), _ptr(acc),
              _ptr(workspace) if ws_bytes else 0, _stream(dev)))
     return Y, acc
+
+
+# ------------------------------------------------------------- 1-bit activations
+BITS_PLAIN, BITS_CODES = 1, 2
+
+
+def pack_weights_binary(W: torch.Tensor, workspace: torch.Tensor | None = None) -> PackedWeight:
+    """bt_pack_weights_binary: sign bits of W [N,K] fp32 and its absmax (W1A1 weights)."""
+    _need(W, "W", torch.float32)
+    N, K = W.shape
+    dev = W.device
+    data = torch.empty(max(int(lib().bt_binary_weight_bytes(N, K)), 16), dtype=torch.uint8, device=dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    ws_bytes = pack_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
+    check(lib().bt_pack_weights_binary(_ptr(W), N, K, _ptr(data), _ptr(scale), _ptr(workspace), _stream(dev)))
+    return PackedWeight(data, scale, N, K)
+
+
+def binarize_act(X: torch.Tensor, layout: int, out=None):
+    """bt_binarize_act: (bits [M, row_bytes / 4] int32, x_scale [M] = absmax per token)."""
+    _need(X, "X", torch.float32)
+    M, K = X.shape
+    dev = X.device
+    if out is None:
+        words = int(lib().bt_act_bits_row_bytes(K, layout)) // 4
+        Xb = torch.empty((M, words), dtype=torch.int32, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+    else:
+        Xb, sx = out
+    check(lib().bt_binarize_act(_ptr(X), M, K, layout, _ptr(Xb), _ptr(sx), _stream(dev)))
+    return Xb, sx
+
+
+def _bits_product(fn_name, pw: PackedWeight, b, want_y, want_acc, out_y, out_acc):
+    Xb, sx = b
+    M = sx.shape[0]
+    dev = pw.data.device
+    Y = out_y if out_y is not None else (
+        torch.empty((M, pw.N), dtype=torch.float32, device=dev) if want_y else None)
+    acc = out_acc if out_acc is not None else (
+        torch.empty((M, pw.N), dtype=torch.int32, device=dev) if want_acc else None)
+    check(getattr(lib(), fn_name)(_ptr(pw.data), _ptr(pw.scale), _ptr(Xb), _ptr(sx), M, pw.N, pw.K, _ptr(Y),
+                                  _ptr(acc), _stream(dev)))
+    return Y, acc
+
+
+def binary_gemv(pw: PackedWeight, b, want_y=True, want_acc=False, out_y=None, out_acc=None):
+    """bt_binary_gemv (W1A1): ``pw`` from pack_weights_binary, ``b`` from binarize_act(X, BITS_PLAIN)."""
+    return _bits_product("bt_binary_gemv", pw, b, want_y, want_acc, out_y, out_acc)
+
+
+def ternary_gemv_a1(pw: PackedWeight, b, want_y=True, want_acc=False, out_y=None, out_acc=None):
+    """bt_ternary_gemv_a1 (W1.58A1): ``pw`` from pack_weights, ``b`` from binarize_act(X, BITS_CODES)."""
+    return _bits_product("bt_ternary_gemv_a1", pw, b, want_y, want_acc, out_y, out_acc)

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libbt.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "lut.hip", "decode.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "lut.hip", "bits.hip", "decode.hip", "gemm.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

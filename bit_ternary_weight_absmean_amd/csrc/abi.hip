@@ -381,6 +381,96 @@ bt_status bt_ternary_linear_rs(const void *Wp, const float *row_scale, const flo
     return linear_impl(Wp, row_scale, true, X, M, N, K, Y, acc, workspace, stream);
 }
 
+size_t bt_binary_weight_bytes(int64_t N, int64_t K)
+{
+    if (N <= 0 || K <= 0)
+        return 0;
+    return (size_t)(bt::round_up(N, 64) * bt::round_up(K, 128) / 8);
+}
+
+int64_t bt_act_bits_row_bytes(int64_t K, int32_t layout)
+{
+    if (K <= 0 || (layout != BT_BITS_PLAIN && layout != BT_BITS_CODES))
+        return 0;
+    return 4 * bt::act_bits_words(K, layout);
+}
+
+bt_status bt_pack_weights_binary(const float *W, int64_t N, int64_t K, void *Wb, float *w_scale, void *workspace,
+                                 void *stream)
+{
+    if (N < 0 || N > (int64_t)1 << 30)
+        return fail(BT_ERR_SHAPE, "N = %lld outside [0, 2^30]", (long long)N);
+    if (bt_status s = check_k(K))
+        return s;
+    if (N == 0 || K == 0)
+        return fail(BT_ERR_SHAPE, "binary packing needs N > 0 and K > 0");
+    if (!W || !Wb || !w_scale || !workspace)
+        return fail(BT_ERR_NULL, "NULL W, Wb, w_scale or workspace");
+    if (!aligned(W, 4) || !aligned(Wb, 16) || !aligned(w_scale, 4) || !aligned(workspace, 8))
+        return fail(BT_ERR_ALIGN, "Wb must be 16-byte aligned; W, w_scale and workspace 4/8-byte aligned");
+    return hip_status(bt::launch_pack_binary(W, N, K, static_cast<uint4 *>(Wb), w_scale,
+                                             static_cast<float *>(workspace), static_cast<hipStream_t>(stream)),
+                      "bt_pack_weights_binary launch");
+}
+
+bt_status bt_binarize_act(const float *X, int64_t M, int64_t K, int32_t layout, uint32_t *Xb, float *x_scale,
+                          void *stream)
+{
+    if (M < 0 || M > (int64_t)1 << 30)
+        return fail(BT_ERR_SHAPE, "M = %lld outside [0, 2^30]", (long long)M);
+    if (bt_status s = check_k(K))
+        return s;
+    if (layout != BT_BITS_PLAIN && layout != BT_BITS_CODES)
+        return fail(BT_ERR_UNSUPPORTED, "unknown bit layout %d", (int)layout);
+    if (M == 0 || K == 0)
+        return fail(BT_ERR_SHAPE, "binarizing needs M > 0 and K > 0");
+    if (!X || !Xb || !x_scale)
+        return fail(BT_ERR_NULL, "NULL X, Xb or x_scale");
+    if (!aligned(X, 4) || !aligned(Xb, 16) || !aligned(x_scale, 4))
+        return fail(BT_ERR_ALIGN, "Xb must be 16-byte aligned; X and x_scale 4-byte aligned");
+    return hip_status(bt::launch_binarize(X, M, K, layout, Xb, x_scale, static_cast<hipStream_t>(stream)),
+                      "bt_binarize_act launch");
+}
+
+static bt_status check_bits_product(const void *Wq, const float *w_scale, const uint32_t *Xb, const float *x_scale,
+                                    int64_t M, int64_t N, int64_t K, const float *Y, const int32_t *acc)
+{
+    if (M < 1 || M > BT_GEMV_MAX_M)
+        return fail(BT_ERR_UNSUPPORTED, "1-bit GEMVs take 1 <= M <= %d (got %lld)", BT_GEMV_MAX_M, (long long)M);
+    if (N < 1 || N > (int64_t)1 << 30)
+        return fail(BT_ERR_SHAPE, "N = %lld outside [1, 2^30]", (long long)N);
+    if (K < 1 || K > BT_MAX_K)
+        return fail(BT_ERR_SHAPE, "K = %lld outside [1, %d]", (long long)K, BT_MAX_K);
+    if (!Y && !acc)
+        return fail(BT_ERR_NULL, "Y and acc are both NULL");
+    if (!Wq || !w_scale || !Xb || !x_scale)
+        return fail(BT_ERR_NULL, "NULL input pointer");
+    if (!aligned(Wq, 16) || !aligned(Xb, 16) || !aligned(w_scale, 4) || !aligned(x_scale, 4) ||
+        (Y && !aligned(Y, 4)) || (acc && !aligned(acc, 4)))
+        return fail(BT_ERR_ALIGN, "weights and bits 16-byte aligned, scales and outputs 4-byte aligned");
+    return BT_OK;
+}
+
+bt_status bt_binary_gemv(const void *Wb, const float *w_scale, const uint32_t *Xb, const float *x_scale, int64_t M,
+                         int64_t N, int64_t K, float *Y, int32_t *acc, void *stream)
+{
+    if (bt_status s = check_bits_product(Wb, w_scale, Xb, x_scale, M, N, K, Y, acc))
+        return s;
+    return hip_status(bt::launch_gemv_binary(static_cast<const uint4 *>(Wb), w_scale, Xb, x_scale, M, N, K, Y, acc,
+                                             static_cast<hipStream_t>(stream)),
+                      "bt_binary_gemv launch");
+}
+
+bt_status bt_ternary_gemv_a1(const void *Wp, const float *w_scale, const uint32_t *Xb, const float *x_scale,
+                             int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *stream)
+{
+    if (bt_status s = check_bits_product(Wp, w_scale, Xb, x_scale, M, N, K, Y, acc))
+        return s;
+    return hip_status(bt::launch_gemv_ternary_a1(static_cast<const uint4 *>(Wp), w_scale, Xb, x_scale, M, N, K, Y,
+                                                 acc, static_cast<hipStream_t>(stream)),
+                      "bt_ternary_gemv_a1 launch");
+}
+
 const char *bt_status_str(bt_status s)
 {
     switch (s) {

@@ -63,6 +63,16 @@ hipError_t launch_gemv_dot4(const uint4 *Wp, const float *w_scale, bool row_scal
 hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq,
                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
                             int32_t *acc, hipStream_t s);
+// 1-bit activations: binary weights (pack, W1A1 GEMV), activation bits (layout 1: plain,
+// 2: aligned with the ternary codes) and the ternary-weight W1.58A1 GEMV.
+int64_t act_bits_words(int64_t K, int layout);
+hipError_t launch_pack_binary(const float *W, int64_t N, int64_t K, uint4 *Wb, float *w_scale, float *rowmax,
+                              hipStream_t s);
+hipError_t launch_binarize(const float *X, int64_t M, int64_t K, int layout, uint32_t *Xb, float *sx, hipStream_t s);
+hipError_t launch_gemv_binary(const uint4 *Wb, const float *w_scale, const uint32_t *Xb, const float *sx, int64_t M,
+                              int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s);
+hipError_t launch_gemv_ternary_a1(const uint4 *Wp, const float *w_scale, const uint32_t *Xb, const float *sx,
+                                  int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s);
 // Table-lookup GEMV for one token; the LDS bytes its tables take.
 hipError_t launch_gemv_lut(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq,
                            const float *sx, const int32_t *xsum, int64_t N, int64_t K, float *Y, int32_t *acc,

@@ -28,8 +28,11 @@ SHAPES_2B = (("qkv", 3840, 2560), ("o", 2560, 2560), ("gate_up", 13824, 2560), (
 SHAPES_7B = (("qkv", 12288, 4096), ("o", 4096, 4096), ("gate_up", 22016, 4096), ("down", 4096, 11008))
 SHAPES_100B = (("qkv", 10240, 8192), ("o", 8192, 8192), ("gate_up", 57344, 8192), ("down", 8192, 28672))
 
+# The 1-bit-activation GEMV shapes the bit-floor page benchmarks: (weight kind, N, K).
+SHAPES_ONEBIT = (("binary", 4096, 4096), ("ternary", 4096, 4096), ("ternary", 11008, 4096))
+
 # Workload ids used for seeding.
-CFG_TINY, CFG_2B_DECODE, CFG_7B_DECODE, CFG_2B_PREFILL, CFG_100B_DECODE = 1, 2, 3, 4, 5
+CFG_TINY, CFG_2B_DECODE, CFG_7B_DECODE, CFG_2B_PREFILL, CFG_100B_DECODE, CFG_ONEBIT = 1, 2, 3, 4, 5, 6
 
 # Row groups of the fused matrices (the model's separate matrices stacked in output-row
 # order): Q, K, V (grouped-query attention: K and V narrower at 2B and 100B) and gate, up.

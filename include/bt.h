@@ -264,6 +264,60 @@ bt_status bt_ternary_linear_rs(const void *Wp, const float *row_scale, const flo
                                int64_t N, int64_t K, float *Y, int32_t *acc, void *workspace,
                                void *stream);
 
+/*
+ * 1-bit activations: the binary GEMV (W1A1) and ternary weights against binarized
+ * tokens (W1.58A1). Follows the "bit-floor" page, "The core math" (binary GEMV =
+ * 2 * POPCNT(XNOR(W, x)) - K over packed sign bits; ternary GEMV = POPCNT(mag &
+ * XNOR(sign, x)) - POPCNT(mag & XOR(sign, x)) over a magnitude and a sign plane) and
+ * "What's inside" (pack.rs: absmax scale for binary weights; scale.rs: activations
+ * binarized before each GEMV). A value v binarizes to +1 when v >= 0 and to -1 when
+ * v < 0; a set bit means -1 in every plane.
+ *
+ * Bit layouts of the activations (rows of bt_act_bits_row_bytes(K, layout) bytes, bits
+ * past K clear):
+ *   BT_BITS_PLAIN  bit b of 32-bit word i is k = 32 i + b (for bt_binary_gemv);
+ *   BT_BITS_CODES  word i holds k = 16 i + b at bit 8 (b % 4) + 2 (b / 4), where code b's
+ *                  low bit sits in a packed ternary word (for bt_ternary_gemv_a1, which
+ *                  reads the weights of bt_pack_weights as they are).
+ */
+#define BT_BITS_PLAIN 1
+#define BT_BITS_CODES 2
+
+/* Binary weight layout: chunks of 64 rows x 128 k, 1024 bytes, chunk (rb, c) at byte
+ * ((rb * ceil(K/128)) + c) * 1024; row r of the chunk is the 16 bytes at 16 r; 32-bit word
+ * j holds k = 128 c + 32 j + b at bit b; padding bits clear. Size Np * Kp / 8 bytes with
+ * Np = N rounded up to 64, Kp = K rounded up to 128. */
+size_t bt_binary_weight_bytes(int64_t N, int64_t K);
+int64_t bt_act_bits_row_bytes(int64_t K, int32_t layout);
+
+/* bt_pack_weights_binary -- sign bits of W [N,K] fp32 (row-major, 4-byte aligned) into
+ * Wb (bt_binary_weight_bytes(N,K) bytes, 16-byte aligned) and w_scale[0] = max |W|
+ * (exact). workspace: bt_pack_workspace_bytes(N,K) bytes, 8-byte aligned. N, K > 0. */
+bt_status bt_pack_weights_binary(const float *W, int64_t N, int64_t K, void *Wb, float *w_scale,
+                                 void *workspace, void *stream);
+
+/* bt_binarize_act -- per token m: x_scale[m] = max_k |X[m,k]| (exact) and the sign bits
+ * of the row in `layout` into Xb (M rows of bt_act_bits_row_bytes(K, layout) bytes,
+ * 16-byte aligned). M, K > 0. */
+bt_status bt_binarize_act(const float *X, int64_t M, int64_t K, int32_t layout, uint32_t *Xb,
+                          float *x_scale, void *stream);
+
+/* bt_binary_gemv -- W1A1 for 1 <= M <= BT_GEMV_MAX_M tokens: acc[m,n] = sum_k
+ * sign(W[n,k]) sign(X[m,k]) = K - 2 * popcount(Wb_n xor Xb_m) (int32, exact) and
+ * Y[m,n] = fp32(acc) * (w_scale[0] * x_scale[m]). Wb from bt_pack_weights_binary, Xb
+ * from bt_binarize_act with BT_BITS_PLAIN. Y or acc may be NULL, not both. */
+bt_status bt_binary_gemv(const void *Wb, const float *w_scale, const uint32_t *Xb,
+                         const float *x_scale, int64_t M, int64_t N, int64_t K, float *Y,
+                         int32_t *acc, void *stream);
+
+/* bt_ternary_gemv_a1 -- W1.58A1 for 1 <= M <= BT_GEMV_MAX_M tokens: acc[m,n] = sum_k
+ * t[n,k] sign(X[m,k]) (int32, exact), from the packed ternary weights of bt_pack_weights
+ * and Xb from bt_binarize_act with BT_BITS_CODES; Y[m,n] = fp32(acc) * (gamma *
+ * x_scale[m]), gamma = w_scale[0]. Y or acc may be NULL, not both. */
+bt_status bt_ternary_gemv_a1(const void *Wp, const float *w_scale, const uint32_t *Xb,
+                             const float *x_scale, int64_t M, int64_t N, int64_t K, float *Y,
+                             int32_t *acc, void *stream);
+
 /* Static text for a status code. */
 const char *bt_status_str(bt_status s);
 
