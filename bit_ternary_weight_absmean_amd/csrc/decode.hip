@@ -31,9 +31,10 @@
 // registers first (they are small and L2-resident), then issues its weight loads,
 // so the quantizer only waits for the activations. It uses the arithmetic of
 // bt_quant_act (a = max |x|, inv = 127.0f / a, q = clamp(rint(x * inv), -127, 127),
-// s_x = a / 127.0f) and stages the int8 tokens in LDS (row pitch Kp + 16 bytes, so
-// the 16-byte operand reads of 16 tokens hit distinct banks, Kp = K rounded up to a whole
-// 256-k step, zero-filled). Within each 64-k chunk the quantizer stores the 4 x 4 dwords
+// s_x = a / 127.0f) and stages the int8 tokens in LDS (row pitch = the bytes the
+// quantizer stores per token, at least K rounded up to a whole 256-k step and zero
+// past K, plus 16 so that the 16-byte operand reads of 16 tokens hit distinct banks; see
+// fused_pitch). Within each 64-k chunk the quantizer stores the 4 x 4 dwords
 // transposed: bytes 16s .. 16s + 15 hold dwords s, s + 4, s + 8, s + 12 of the chunk, the
 // B operand of mask s, so each operand is one 16-byte LDS read with no register moves.
 // Slots outside the matrix need no masking there: weight chunks past K (clamped

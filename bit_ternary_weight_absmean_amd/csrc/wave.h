@@ -1,6 +1,8 @@
-// Wave64 reductions on gfx950 without LDS traffic: DPP within each 16-lane row
-// (quad swaps, half-row mirror, row mirror), then v_permlane16_swap and
-// v_permlane32_swap to combine the four rows. Every lane ends with the result.
+// Device helpers shared by the kernels: wave64 reductions on gfx950 without LDS traffic
+// (DPP within each 16-lane row -- quad swaps, half-row mirror, row mirror -- then
+// v_permlane16_swap and v_permlane32_swap to combine the four rows; every lane ends with
+// the result), the per-token int8 quantizer of four values, and vector-memory reads of
+// the weight scales.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -51,31 +53,15 @@ __device__ inline int wave_sum_i32(int v)
     return (int)wave_reduce_bits((uint32_t)v, [](uint32_t a, uint32_t b) { return (uint32_t)((int)a + (int)b); });
 }
 
-// Per-token int8 quantization of one value (the rule of bt_quant_act).
-__device__ inline int quant_one(float x, float inv)
-{
-    float r = rintf(x * inv);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
-}
-
-__device__ inline uint32_t quant_pack4(float4 v, float inv)
-{
-    const int e0 = quant_one(v.x, inv), e1 = quant_one(v.y, inv), e2 = quant_one(v.z, inv),
-              e3 = quant_one(v.w, inv);
-    return (uint32_t)(e0 & 0xff) | ((uint32_t)(e1 & 0xff) << 8) | ((uint32_t)(e2 & 0xff) << 16) |
-           ((uint32_t)(e3 & 0xff) << 24);
-}
-
-// The same quantization of four values in fewer instructions, with the sum of the four
+// Per-token int8 quantization of four values (the rule of bt_quant_act), with the sum of the four
 // codes. Both steps of the rule are kept exactly:
 //  * p = x * inv rounded to fp32 (its own instruction, never contracted into an FMA);
 //  * p + 1.5 * 2^23 lands in [2^23, 2^24), where the fp32 spacing is 1, so the addition
 //    rounds p to the nearest integer with ties to even (rintf) and leaves q in the low
 //    mantissa bits: bits = 0x4B400000 + q, low byte = q as int8.
 // The clamp to +-127 is dropped because it never applies: with inv = RN(127 / a) and
-// |x| <= a, |p| <= 127 * (1 + 2^-24) rounds to at most 127 (finite inputs; a = 0 gives
-// inv = 0 and q = 0).
+// |x| <= a, |x * inv| <= 127 * (1 + 2^-24), so p is at most one ulp above 127 in
+// magnitude and still rounds to +-127 (finite inputs; a = 0 gives inv = 0 and q = 0).
 constexpr float kQuantMagic = 12582912.0f;  // 1.5 * 2^23
 constexpr uint32_t kQuantMagicBits = 0x4B400000u;
 
@@ -120,12 +106,6 @@ __device__ inline float4 load_scales4(const float *w_scale, int64_t n, int64_t N
                        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off + step, 0, 0)),
                        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off + 2 * step, 0, 0)),
                        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off + 3 * step, 0, 0)));
-}
-
-__device__ inline int sum_bytes_s8(uint32_t p)
-{
-    return (int)(int8_t)(p & 0xff) + (int)(int8_t)((p >> 8) & 0xff) + (int)(int8_t)((p >> 16) & 0xff) +
-           (int)(int8_t)(p >> 24);
 }
 
 }  // namespace bt
