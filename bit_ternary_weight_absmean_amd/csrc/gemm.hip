@@ -29,8 +29,9 @@
 //    substep-0 operands are then read while this step's substep-1 MFMAs run.
 //  * output: lane holds D[4g + v][r] of each tile = token 16a + 4g + v, weight row
 //    16i + r; the wave transposes its tile through LDS 16 tokens at a time and stores
-//    y = (acc - sum_k q) * (gamma * s_x) row-contiguously, 16 bytes per lane, with
-//    non-temporal stores.
+//    y = (acc - sum_k q) * (gamma_n * s_x) row-contiguously, 16 bytes per lane, with
+//    non-temporal stores (gamma_n: the matrix's gamma, or weight row n's scale with row
+//    scales; the workgroup's BN scales wait in LDS with the row statistics).
 //  * workgroup -> tile map is XCD-aware: consecutive workgroup ids land on different
 //    XCDs, so each XCD is given a contiguous run of a grouped tile order (8 token-tile
 //    rows walked weight-tile column by column): the workgroups resident on an XCD then
