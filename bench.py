@@ -57,6 +57,7 @@ CSRC = os.path.join(ROOT, "bit_ternary_weight_absmean_amd", "csrc")
 KERNEL_SOURCES = {
     "k_linear_decode": ["decode.hip", "wave.h", "bt_internal.h"],
     "k_gemv_direct": ["decode.hip", "wave.h", "bt_internal.h"],
+    "k_gemv_staged": ["decode.hip", "wave.h", "bt_internal.h"],
     "k_gemv_dot4": ["gemv.hip", "bt_internal.h"],
     "k_gemv_lut": ["lut.hip", "bt_internal.h"],
     "k_gemm": ["gemm.hip", "bt_internal.h"],
@@ -73,8 +74,8 @@ def parse():
     p.add_argument("--m", type=int, default=None, help="tokens per call (default: 1 for decode, 2048 for prefill)")
     p.add_argument("--eager", action="store_true", help="launch kernels one by one instead of replaying graphs")
     p.add_argument("--split", action="store_true", help="time bt_quant_act + product as two launches per matrix")
-    p.add_argument("--gemv-algo", choices=("mfma", "dot4", "lut"), default="mfma",
-                   help="with --split at M <= 16: the decode product kernel (bt_ternary_gemv_algo)")
+    p.add_argument("--gemv-algo", choices=("auto", "mfma", "staged", "dot4", "lut"), default="auto",
+                   help="at M <= 16 on the unfused route: the decode product kernel (bt_ternary_gemv_algo)")
     p.add_argument("--row-scales", action="store_true",
                    help="row-group weight scales: fused Q/K/V and gate/up matrices packed with one scale per "
                         "block (bt_pack_weights_rows), products through the row-scale entry points")
@@ -198,8 +199,14 @@ def run_gpu(args, spec):
     elif spec["prefill"] or M > bt.GEMV_MAX_M:
         kernel = "k_gemm"
     else:
-        kernel = {"mfma": "k_gemv_direct", "dot4": "k_gemv_dot4", "lut": "k_gemv_lut"}[args.gemv_algo]
-    algo = {"mfma": bt.GEMV_MFMA, "dot4": bt.GEMV_DOT4, "lut": bt.GEMV_LUT}[args.gemv_algo]
+        names = {"mfma": "k_gemv_direct", "staged": "k_gemv_staged", "dot4": "k_gemv_dot4", "lut": "k_gemv_lut"}
+        if args.gemv_algo == "auto":  # the library's pick per shape (BT_GEMV_AUTO), as bt_ternary_linear makes it
+            picks = ["staged" if M >= 5 and M * ((K + 255) // 256 * 256) <= 131072 else "mfma" for _, _, K in shapes]
+            kernel = " + ".join(dict.fromkeys(names[c] for c in picks))
+        else:
+            kernel = names[args.gemv_algo]
+    algo = {"auto": bt.GEMV_AUTO, "mfma": bt.GEMV_MFMA, "staged": bt.GEMV_STAGED, "dot4": bt.GEMV_DOT4,
+            "lut": bt.GEMV_LUT}[args.gemv_algo]
 
     def product(pw, q, out_y, j):
         if kernel == "k_gemm":

@@ -18,6 +18,7 @@ from .api import (
     GEMV_LUT,
     GEMV_MAX_M,
     GEMV_MFMA,
+    GEMV_STAGED,
     PackedWeight,
     act_row_bytes,
     binarize_act,
@@ -40,7 +41,7 @@ from .api import (
 
 __all__ = [
     "BITS_CODES", "BITS_PLAIN", "binarize_act", "binary_gemv", "pack_weights_binary", "ternary_gemv_a1",
-    "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_LUT", "GEMV_MFMA", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
+    "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_LUT", "GEMV_MFMA", "GEMV_STAGED", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
     "gemm_workspace", "gemm_workspace_bytes", "linear", "linear_workspace_bytes", "pack_weights", "pack_weights_rows", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
     "ternary_gemv", "unpack_weights",
 ]

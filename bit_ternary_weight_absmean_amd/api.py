@@ -13,7 +13,7 @@ import torch
 
 from ._lib import check, lib
 
-GEMV_AUTO, GEMV_DOT4, GEMV_MFMA, GEMV_LUT = 0, 1, 2, 3
+GEMV_AUTO, GEMV_DOT4, GEMV_MFMA, GEMV_LUT, GEMV_STAGED = 0, 1, 2, 3, 4
 GEMV_MAX_M = 16
 
 

@@ -200,12 +200,19 @@ static bt_status gemv_impl(const void *Wp, const float *w_scale, bool rows, cons
     if (M > BT_GEMV_MAX_M)
         return fail(BT_ERR_UNSUPPORTED, "gemv takes M <= %d (got %lld); use bt_ternary_gemm", BT_GEMV_MAX_M,
                     (long long)M);
-    if (algo != BT_GEMV_AUTO && algo != BT_GEMV_DOT4 && algo != BT_GEMV_MFMA && algo != BT_GEMV_LUT)
+    if (algo != BT_GEMV_AUTO && algo != BT_GEMV_DOT4 && algo != BT_GEMV_MFMA && algo != BT_GEMV_LUT &&
+        algo != BT_GEMV_STAGED)
         return fail(BT_ERR_UNSUPPORTED, "unknown gemv algo %d", (int)algo);
     if (M == 0 || N == 0)
         return ok();
     if (algo == BT_GEMV_AUTO)
-        algo = BT_GEMV_MFMA;
+        algo = (M >= 5 && bt::gemv_staged_fits(M, N, K)) ? BT_GEMV_STAGED : BT_GEMV_MFMA;
+    if (algo == BT_GEMV_STAGED) {
+        if (K == 0)
+            algo = BT_GEMV_MFMA;
+        else if (!bt::gemv_staged_fits(M, N, K))
+            return fail(BT_ERR_UNSUPPORTED, "staged gemv takes M <= 16 with M * K (rounded up to 256) <= 131072");
+    }
     if (algo == BT_GEMV_DOT4 && M > 4)
         return fail(BT_ERR_UNSUPPORTED, "dot4 gemv takes M <= 4 (got %lld)", (long long)M);
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -226,6 +233,8 @@ static bt_status gemv_impl(const void *Wp, const float *w_scale, bool rows, cons
     const uint4 *W = static_cast<const uint4 *>(Wp);
     hipError_t e = (algo == BT_GEMV_DOT4)
                        ? bt::launch_gemv_dot4(W, w_scale, rows, Xq, ldq, x_scale, x_sum, M, N, K, Y, acc, s)
+                   : (algo == BT_GEMV_STAGED)
+                       ? bt::launch_gemv_staged(W, w_scale, rows, Xq, x_scale, x_sum, M, N, K, Y, acc, s)
                    : (algo == BT_GEMV_LUT)
                        ? bt::launch_gemv_lut(W, w_scale, rows, Xq, x_scale, x_sum, N, K, Y, acc, s)
                        : bt::launch_gemv_mfma(W, w_scale, rows, Xq, ldq, x_scale, x_sum, M, N, K, Y, acc, s);
@@ -300,7 +309,7 @@ static bt_status linear_impl(const void *Wp, const float *w_scale, bool rows, co
     if (M <= BT_GEMV_MAX_M) {
         if (bt_status st = bt_quant_act(X, M, K, Xq, sx, xsum, stream))
             return st;
-        return gemv_impl(Wp, w_scale, rows, Xq, sx, xsum, M, N, K, Y, acc, BT_GEMV_MFMA, stream);
+        return gemv_impl(Wp, w_scale, rows, Xq, sx, xsum, M, N, K, Y, acc, BT_GEMV_AUTO, stream);
     }
     // The quantizer also zero-fills the split-K arrival counters of the GEMM workspace,
     // so the caller's workspace needs no initialization.

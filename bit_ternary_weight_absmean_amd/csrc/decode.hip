@@ -685,6 +685,165 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     }
 }
 
+// ------------------------------------------------------------- staged kernel
+// Pre-quantized activations for 5 <= M <= 16 tokens (bt_ternary_gemv, and the unfused
+// route of bt_ternary_linear): the fused kernel's streaming design -- eight waves, k-splits
+// S, two weight batches in flight, every MFMA B operand one 16-byte LDS read -- with its
+// quantizer replaced by a copy of the int8 rows (bt_act_row_bytes(K) bytes each, zero past
+// K) into the same transposed chunk layout. The activations then cross the L2 once per
+// workgroup instead of once per step and row block (k_gemv_direct). Each thread copies at
+// most CH 64-byte chunks (CH = 2 up to 64 KB of staged rows, 4 up to 128 KB): its loads go
+// out first, then the weights', so the copy waits for the activations only.
+constexpr int kStagedMaxChunks = 4;
+
+template <int MT, int S, int U, bool ROWS, int CH>
+__global__ __launch_bounds__(kFusedWaves * 64) void k_gemv_staged(
+    const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq,
+    float *__restrict__ Y, int32_t *__restrict__ ACC, int M, int N, int K, const float *__restrict__ sx_in,
+    const int32_t *__restrict__ xsum_in)
+{
+    constexpr int WAVES = kFusedWaves;
+    constexpr int T = WAVES * 64;
+    constexpr int RBW = WAVES / S;
+    constexpr int KE = S - 1;  // the k-split that runs the epilogue (it owns the fewest steps)
+    const int KC = (K + 63) >> 6;
+    const int NB16 = ((N + 63) >> 6) * 4;
+    const int KC4 = (KC + 3) & ~3;
+    const int ldq = KC4 * 64;  // K rounded up to 256: the Xq row stride
+    const int pitch = fused_pitch(KC4, 0);
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    int4 *red = reinterpret_cast<int4 *>(smem);  // [WAVES][64] (S > 1)
+    int8_t *xq = reinterpret_cast<int8_t *>(smem + (S > 1 ? WAVES * 64 * 16 : 0));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int g = lane >> 4;
+    const int r = lane & 15;
+    const int ks = wave % S;
+    const int b16 = blockIdx.x * RBW + wave / S;
+
+    // 1. The activation chunks (token m, 64-k chunk c), at clamped valid addresses.
+    const int nchunks = M * KC4;
+    v4i cb[CH][4];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int ch = min(tid + i * T, nchunks - 1);
+        const int m = ch / KC4, c = ch - m * KC4;
+        const v4i *src = reinterpret_cast<const v4i *>(Xq + (int64_t)m * ldq + c * 64);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            cb[i][q] = src[q];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. The wave's first two weight batches, then the epilogue's inputs.
+    const int nsteps = (KC + 3) >> 2;
+    const int nmine = (ks < nsteps) ? (nsteps - 1 - ks) / S + 1 : 0;
+    const int nb = (nmine + U - 1) / U;
+    v4i wa[U], wb[U];
+    auto load_batch = [&](v4i (&w)[U], int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            w[u] = load_w_raw(Wp, b16, NB16, 4 * (ks + S * (b * U + u)) + g, KC, r);
+    };
+    load_batch(wa, 0);  // K >= 1: valid clamped addresses
+    load_batch(wb, 1);
+    float4 gam;
+    if constexpr (ROWS) {
+        gam = load_scales4(w_scale, (int64_t)b16 * 16 + 4 * g, N, true);
+    } else {
+        const float g1 = load_scale_vmem(w_scale);
+        gam = make_float4(g1, g1, g1, g1);
+    }
+    const int rt = min(r, M - 1);  // token of this lane's output column
+    const float sx_r = sx_in[rt];
+    const int qs_r = xsum_in[rt];
+
+    // 3. Into LDS, transposed within each chunk: bytes 16s .. 16s + 15 take dwords
+    //    s, s + 4, s + 8, s + 12 (the B operand of mask s).
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int ch = tid + i * T;
+        if (ch < nchunks) {
+            const int m = ch / KC4, c = ch - m * KC4;
+            v4i *dst = reinterpret_cast<v4i *>(xq + m * pitch + c * 64);
+#pragma unroll
+            for (int sidx = 0; sidx < 4; ++sidx)
+                dst[sidx] = v4i{cb[i][0][sidx], cb[i][1][sidx], cb[i][2][sidx], cb[i][3][sidx]};
+        }
+    }
+    __syncthreads();
+
+    // 4. Stream the wave's weights, two batches in flight, MFMAs on the older one. Token
+    //    columns r >= M read token M - 1 (never stored); chunks read lie in the rows.
+    v4i a1 = v4i{0, 0, 0, 0}, a4 = a1, a16 = a1;
+    const int8_t *xrow = xq + rt * pitch;
+    auto compute_batch = [&](const v4i (&w)[U], int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = b * U + u;
+            if (i < nmine) {
+                const v4i *p = reinterpret_cast<const v4i *>(xrow + (4 * (ks + S * i) + g) * 64);
+                const v4i bo[4] = {p[0], p[1], p[2], p[3]};
+                mfma_step_t(w[u], bo, a1, a4, a16);
+            }
+        }
+    };
+    for (int b = 0; b < nb; b += 2) {
+        compute_batch(wa, b);
+        if (b + 2 < nb)
+            load_batch(wa, b + 2);
+        if (b + 1 < nb) {
+            compute_batch(wb, b + 1);
+            if (b + 3 < nb)
+                load_batch(wb, b + 3);
+        }
+    }
+
+    // 5. k-split sum (S > 1) and the epilogue; lane (g, r) holds rows 4g + v for token r.
+    int part[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        part[v] = a1[v] + (a4[v] >> 2) + (a16[v] >> 4);
+    if constexpr (S > 1) {
+        if (ks != KE)
+            red[wave * 64 + lane] = make_int4(part[0], part[1], part[2], part[3]);
+        __syncthreads();
+        if (ks == KE) {
+#pragma unroll
+            for (int j = 0; j < KE; ++j) {
+                const int4 o = red[(wave - KE + j) * 64 + lane];
+                part[0] += o.x, part[1] += o.y, part[2] += o.z, part[3] += o.w;
+            }
+        }
+    }
+    if (ks == KE && r < M) {
+        const float sc[4] = {gam.x * sx_r, gam.y * sx_r, gam.z * sx_r, gam.w * sx_r};
+        const int64_t n0 = (int64_t)b16 * 16 + 4 * g;
+        if ((N & 3) == 0 && n0 < N && ((reinterpret_cast<uintptr_t>(Y) | reinterpret_cast<uintptr_t>(ACC)) & 15) == 0) {
+            const int4 acc = make_int4(part[0] - qs_r, part[1] - qs_r, part[2] - qs_r, part[3] - qs_r);
+            if (ACC)
+                *reinterpret_cast<int4 *>(ACC + (int64_t)r * N + n0) = acc;
+            if (Y)
+                *reinterpret_cast<float4 *>(Y + (int64_t)r * N + n0) =
+                    make_float4((float)acc.x * sc[0], (float)acc.y * sc[1], (float)acc.z * sc[2], (float)acc.w * sc[3]);
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t n = n0 + v;
+                if (n < N) {
+                    const int acc = part[v] - qs_r;
+                    if (ACC)
+                        ACC[(int64_t)r * N + n] = acc;
+                    if (Y)
+                        Y[(int64_t)r * N + n] = (float)acc * sc[v];
+                }
+            }
+        }
+    }
+}
+
 int pick_rb(int64_t N)
 {
     const int64_t nb16 = (N + 15) / 16;
@@ -801,6 +960,65 @@ hipError_t launch_fused_mt(const uint4 *Wp, const float *w_scale, bool row_scale
     }
 }
 
+size_t staged_lds(int64_t M, int64_t K, int s)
+{
+    const int KC4 = (int)(((K + 63) / 64 + 3) / 4 * 4);
+    return (s > 1 ? kFusedWaves * 64 * 16 : 0) + (size_t)M * fused_pitch(KC4, 0);
+}
+
+template <int MT, int S, int U, int CH>
+hipError_t launch_staged_ch(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, const float *sx,
+                            const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
+{
+    constexpr int RBW = kFusedWaves / S;
+    const int64_t nb16 = (N + 15) / 16;
+    const dim3 grid((unsigned)((nb16 + RBW - 1) / RBW)), block(kFusedWaves * 64);
+    if (row_scales)
+        hipLaunchKernelGGL((k_gemv_staged<MT, S, U, true, CH>), grid, block, staged_lds(M, K, S), s, Wp, w_scale, Xq,
+                           Y, acc, (int)M, (int)N, (int)K, sx, xsum);
+    else
+        hipLaunchKernelGGL((k_gemv_staged<MT, S, U, false, CH>), grid, block, staged_lds(M, K, S), s, Wp, w_scale, Xq,
+                           Y, acc, (int)M, (int)N, (int)K, sx, xsum);
+    return hipGetLastError();
+}
+
+// Chunks per thread: the staged rows' 64-byte chunks over the workgroup's threads.
+template <int MT, int S, int U>
+hipError_t launch_staged_u(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, const float *sx,
+                           const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
+{
+    const int64_t nchunks = M * (((K + 63) / 64 + 3) / 4 * 4);
+    if (nchunks <= 2 * kFusedWaves * 64)
+        return launch_staged_ch<MT, S, U, 2>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    return launch_staged_ch<MT, S, U, 4>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+}
+
+template <int MT, int S>
+hipError_t launch_staged_s(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, const float *sx,
+                           const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
+{
+    const int64_t mine = ((K + 255) / 256 + S - 1) / S;
+    if (mine <= 2)
+        return launch_staged_u<MT, S, 1>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    if (mine <= 4)
+        return launch_staged_u<MT, S, 2>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    if (mine <= 6)
+        return launch_staged_u<MT, S, 3>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    return launch_staged_u<MT, S, 4>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+}
+
+template <int MT>
+hipError_t launch_staged_mt(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, const float *sx,
+                            const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
+{
+    switch (pick_s(N)) {
+    case 1: return launch_staged_s<MT, 1>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    case 2: return launch_staged_s<MT, 2>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    case 4: return launch_staged_s<MT, 4>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    default: return launch_staged_s<MT, 8>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    }
+}
+
 template <int RB>
 hipError_t launch_direct_t(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq, const float *sx,
                            const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
@@ -829,6 +1047,28 @@ hipError_t launch_direct_t(const uint4 *Wp, const float *w_scale, bool row_scale
 
 // An upper bound for any activation alignment: the register path's pitch is the larger.
 size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K) { return fused_lds(M, K, pick_s(N), fused_rx(M, K)); }
+
+// The staged kernel takes up to 16 tokens whose int8 rows fit kStagedLdsLimit bytes of LDS
+// (each thread then copies at most kStagedMaxChunks chunks; with the k-split area and the
+// row padding a workgroup stays within the 160 KB of one CU).
+constexpr size_t kStagedLdsLimit = (size_t)kStagedMaxChunks * kFusedWaves * 64 * 64;
+
+bool gemv_staged_fits(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t KC4 = ((K + 63) / 64 + 3) / 4 * 4;
+    return M >= 1 && M <= 16 && K >= 1 && M * KC4 * 64 <= (int64_t)kStagedLdsLimit;
+}
+
+hipError_t launch_gemv_staged(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq,
+                              const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
+                              int32_t *acc, hipStream_t s)
+{
+    if (!gemv_staged_fits(M, N, K))
+        return hipErrorInvalidValue;
+    if (M <= 8)
+        return launch_staged_mt<8>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    return launch_staged_mt<16>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+}
 
 hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq,
                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,

@@ -62,6 +62,10 @@ typedef int32_t bt_status;
 #define BT_GEMV_AUTO 0 /* pick by M from the library's launch table             */
 #define BT_GEMV_DOT4 1 /* one lane per weight row, v_dot4 with the x chunk in SGPRs */
 #define BT_GEMV_MFMA 2 /* int8 MFMA 16x16x64, 64 weight rows per wave             */
+#define BT_GEMV_STAGED 4 /* int8 MFMA with the int8 activations staged once per workgroup
+                            in LDS: M <= 16 with M * (K rounded up to 256) <= 131072
+                            bytes, else BT_ERR_UNSUPPORTED (BT_GEMV_AUTO picks it from
+                            5 tokens on when it fits, BT_GEMV_MFMA otherwise) */
 #define BT_GEMV_LUT 3  /* table lookup (T-MAC / TL1 style): M == 1 only, and K small
                           enough for its LDS tables (16 bytes per k; the device's
                           per-workgroup LDS limit), else BT_ERR_UNSUPPORTED      */
@@ -169,7 +173,7 @@ bt_status bt_ternary_gemv(const void *Wp, const float *w_scale, const int8_t *Xq
                           const float *x_scale, const int32_t *x_sum, int64_t M, int64_t N,
                           int64_t K, float *Y, int32_t *acc, void *stream);
 
-/* bt_ternary_gemv with an explicit kernel choice (BT_GEMV_AUTO / _DOT4 / _MFMA / _LUT).
+/* bt_ternary_gemv with an explicit kernel choice (BT_GEMV_AUTO / _DOT4 / _MFMA / _STAGED / _LUT).
  * BT_GEMV_DOT4 takes M <= 4, BT_GEMV_LUT M == 1; all return bit-identical acc and Y.
  * The table-lookup kernel follows the "Run 100B Models on Your Laptop CPU" page, "What is
  * Microsoft BitNet?" (kernels on T-MAC's lookup-table method) and "Key Features That Make
