@@ -43,6 +43,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -137,10 +138,16 @@ def quant_bytes(M, K):
 
 
 def source_hash(kernel):
+    """SHA-256 of the kernel's sources with comments, indentation and blank lines taken out:
+    counter figures stay valid across comment edits and are dropped on any code change."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            text = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].strip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

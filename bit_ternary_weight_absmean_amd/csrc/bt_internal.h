@@ -78,7 +78,7 @@ hipError_t launch_gemv_lut(const uint4 *Wp, const float *w_scale, bool row_scale
                            const float *sx, const int32_t *xsum, int64_t N, int64_t K, float *Y, int32_t *acc,
                            hipStream_t s);
 size_t gemv_lut_lds_bytes(int64_t K);
-// Pre-quantized activations staged in LDS (1 <= M <= 16 with the int8 rows within 64 KB).
+// Pre-quantized activations staged in LDS (1 <= M <= 16 with the int8 rows within 128 KB).
 bool gemv_staged_fits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv_staged(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq,
                               const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
