@@ -23,6 +23,7 @@ from .api import (
     act_row_bytes,
     binarize_act,
     binary_gemv,
+    gemm_split_plan,
     gemm_workspace,
     gemm_workspace_bytes,
     linear,
@@ -42,6 +43,6 @@ from .api import (
 __all__ = [
     "BITS_CODES", "BITS_PLAIN", "binarize_act", "binary_gemv", "pack_weights_binary", "ternary_gemv_a1",
     "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_LUT", "GEMV_MFMA", "GEMV_STAGED", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
-    "gemm_workspace", "gemm_workspace_bytes", "linear", "linear_workspace_bytes", "pack_weights", "pack_weights_rows", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
+    "gemm_split_plan", "gemm_workspace", "gemm_workspace_bytes", "linear", "linear_workspace_bytes", "pack_weights", "pack_weights_rows", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
     "ternary_gemv", "unpack_weights",
 ]

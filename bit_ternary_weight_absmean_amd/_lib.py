@@ -21,6 +21,7 @@ SIGNATURES = {
     "bt_ternary_gemv_algo": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _i32, _vp]),
     "bt_ternary_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "bt_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bt_gemm_split_plan": (_i32, [_i64, _i64, _i64, _vp, _vp]),
     "bt_ternary_gemm_ws": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
     "bt_linear_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bt_ternary_linear": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),

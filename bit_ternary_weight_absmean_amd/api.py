@@ -146,6 +146,15 @@ def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib().bt_gemm_workspace_bytes(M, N, K))
 
 
+def gemm_split_plan(M: int, N: int, K: int) -> tuple[int, int]:
+    """bt_gemm_split_plan: (full_tiles, splits) -- the first full_tiles 64 x 256 output tiles
+    are computed whole, each later one over `splits` workgroups (splits == 1: no split)."""
+    full = ctypes.c_int64(0)
+    splits = ctypes.c_int32(0)
+    check(lib().bt_gemm_split_plan(M, N, K, ctypes.byref(full), ctypes.byref(splits)))
+    return int(full.value), int(splits.value)
+
+
 def gemm_workspace(M: int, N: int, K: int, device) -> torch.Tensor | None:
     """A zero-filled workspace for bt_ternary_gemm_ws(M, N, K), or None when the shape does not split."""
     n = gemm_workspace_bytes(M, N, K)

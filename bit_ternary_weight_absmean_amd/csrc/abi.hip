@@ -317,7 +317,7 @@ static bt_status linear_impl(const void *Wp, const float *w_scale, bool rows, co
     const size_t gbytes = bt_gemm_workspace_bytes(M, N, K);
     if (bt_status st = hip_status(bt::launch_quant_act(X, M, K, bt_act_row_bytes(K), Xq, sx, xsum,
                                                        reinterpret_cast<unsigned *>(gws),
-                                                       gbytes ? bt::gemm_arrival_words(M, N) : 0, s),
+                                                       gbytes ? bt::gemm_arrival_words(M, N, K) : 0, s),
                                   "bt_quant_act launch"))
         return st;
     return gemm_impl(Wp, w_scale, rows, Xq, sx, xsum, M, N, K, Y, acc, gbytes ? gws : nullptr, gbytes, stream);
@@ -348,6 +348,21 @@ size_t bt_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
     if (M <= 0 || N <= 0 || K <= 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > BT_MAX_K)
         return 0;
     return bt::gemm_workspace_bytes(M, N, K);
+}
+
+bt_status bt_gemm_split_plan(int64_t M, int64_t N, int64_t K, int64_t *full_tiles, int32_t *splits)
+{
+    if (!full_tiles || !splits)
+        return fail(BT_ERR_NULL, "full_tiles and splits must not be NULL");
+    if (M < 0 || N < 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30)
+        return fail(BT_ERR_SHAPE, "shape M = %lld, N = %lld out of range", (long long)M, (long long)N);
+    if (bt_status s = check_k(K))
+        return s;
+    const int64_t tiles = bt::gemm_tiles(M, N);
+    const bt::GemmPlan pl = (M > 0 && N > 0 && K > 0) ? bt::gemm_plan(M, N, K) : bt::GemmPlan{tiles, 1};
+    *full_tiles = pl.nsplit == 1 ? tiles : pl.full;
+    *splits = pl.nsplit;
+    return ok();
 }
 
 bt_status bt_ternary_gemm_ws(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,

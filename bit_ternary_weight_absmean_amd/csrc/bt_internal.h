@@ -88,12 +88,18 @@ hipError_t launch_linear_decode(const uint4 *Wp, const float *w_scale, bool row_
                                 int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s);
 size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K);
 // Prefill GEMM. With a workspace of at least gemm_workspace_bytes(M, N, K) bytes whose
-// first gemm_arrival_words(M, N) words are zero, shapes that gain from it split K over
-// gemm_splits(M, N, K) workgroups per tile (the words are zero again afterwards);
-// otherwise (NULL or smaller workspace) one workgroup per tile.
-int gemm_splits(int64_t M, int64_t N, int64_t K);
+// first gemm_arrival_words(M, N, K) words are zero, shapes that gain from it split the K
+// range of their tiles after the first `full` over `nsplit` workgroups each (gemm_plan;
+// the words are zero again afterwards); otherwise (NULL or smaller workspace) one
+// workgroup per tile.
+struct GemmPlan {
+    int64_t full;  // tiles computed whole (the first ones of the tile order)
+    int nsplit;    // workgroups per later tile; 1: no split at all
+};
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K);
+int64_t gemm_tiles(int64_t M, int64_t N);  // 64 x 256 output tiles
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
-int64_t gemm_arrival_words(int64_t M, int64_t N);
+int64_t gemm_arrival_words(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq,
                        const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
                        void *workspace, size_t workspace_bytes, hipStream_t s);

@@ -37,6 +37,7 @@
 //    rows walked weight-tile column by column): the workgroups resident on an XCD then
 //    share 8 activation panels and a few weight panels in its L2, instead of streaming a
 //    different weight panel each from HBM.
+#include <algorithm>
 #include <type_traits>
 
 #include "bt_internal.h"
@@ -51,6 +52,8 @@ constexpr int kXcds = 8;
 #define BT_GEMM_GROUP 8
 #endif
 constexpr int kGroup = BT_GEMM_GROUP;
+// Fewest 128-k steps a share of a tail-split tile keeps.
+constexpr int64_t kMinTailSteps = 12;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -93,12 +96,12 @@ constexpr int kPartialBytes = BM * BN * 4;
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kSc1 = 1 << 4;
 
-template <int BM, int BN, int WM, int WN, int NS, int WPE, int SPLIT>
+template <int BM, int BN, int WM, int WN, int NS, int WPE, bool SPLITK>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void k_gemm(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
     const float *__restrict__ sx, const int32_t *__restrict__ xsum, int64_t M, int64_t N, int KC, int NBLK,
     int tiles_m, int tiles_n, int group, float *__restrict__ Y, int32_t *__restrict__ ACC, int flags,
-    char *__restrict__ partials, unsigned *__restrict__ arrivals, int per_xcd)
+    char *__restrict__ partials, unsigned *__restrict__ arrivals, int full, int nsplit, int full_x, int split_x)
 {
     // flags bit 0: 16-byte output stores; bit 1: w_scale holds one scale per output row.
     const int vec = flags & 1;
@@ -131,21 +134,36 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     const int wm = wave % WM, wn = wave / WM;
     const int g = lane >> 4, r = lane & 15;
 
-    // Work order. Workgroup b runs on XCD b % 8, and each XCD takes a contiguous run of
-    // per_xcd work items (a multiple of SPLIT): item = tile * SPLIT + split, so the splits
-    // of a tile run side by side on one XCD. Tiles follow a grouped list: groups of
-    // `group` token-tile rows, walked weight-tile column by column, so the workgroups
-    // resident on one XCD at a time cover a compact block of tiles whose activation and
-    // weight panels are shared in that XCD's L2.
+    // Work order. The first `full` tiles of the tile list are computed whole; each later
+    // tile is split over `nsplit` workgroups, each taking a contiguous share of its k-steps
+    // (SPLITK only). Workgroup b runs on XCD b % 8 and is the (b / 8)-th of that XCD: every
+    // XCD takes a contiguous run of full_x whole tiles, then of split_x split tiles with
+    // their nsplit shares side by side (the shares of a tile meet in one XCD's L2). Tiles
+    // follow a grouped list: groups of `group` token-tile rows, walked weight-tile column
+    // by column, so the workgroups resident on one XCD at a time cover a compact block of
+    // tiles whose activation and weight panels are shared in that XCD's L2.
     const int total = tiles_m * tiles_n;
     const int b = blockIdx.x;
-    const int item = (b % kXcds) * per_xcd + b / kXcds;
-    const int t = item / SPLIT, split = item % SPLIT;
-    if (t >= total)
-        return;
-    // This split's 128-k steps: [step0, step0 + nsteps) of the tile's ceil(KC / 2).
+    const int xcd = b % kXcds, j = b / kXcds;
+    int t, split = 0, nsp = 1;
+    if (j < full_x) {
+        t = xcd * full_x + j;
+        if (t >= full)
+            return;
+    } else {
+        if constexpr (!SPLITK)
+            return;
+        const int p = j - full_x;
+        const int ts = xcd * split_x + p / nsplit;  // index among the split tiles
+        if (ts >= total - full)
+            return;
+        t = full + ts;
+        split = p % nsplit;
+        nsp = nsplit;
+    }
+    // This share's 128-k steps: [step0, step0 + nsteps) of the tile's ceil(KC / 2).
     const int nsteps_all = (KC + 1) / 2;
-    const int per_split = (nsteps_all + SPLIT - 1) / SPLIT;
+    const int per_split = (nsteps_all + nsp - 1) / nsp;
     const int step0 = min(split * per_split, nsteps_all);
     const int nsteps = min(per_split, nsteps_all - step0);
     const int last = nsteps - 1;
@@ -344,7 +362,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
 
-    if constexpr (SPLIT > 1) {
+    if (SPLITK && nsp > 1) {
         // Split-K hand-off, with no workgroup ever waiting for another: every split stores
         // its int32 partial tile (the MFMA layout, 16 bytes per lane per 16 x 16 tile) with
         // device-coherent stores (sc1: visible to every XCD once performed, so no L2
@@ -356,7 +374,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
         constexpr int kSlotBytes = kPartialBytes<BM, BN>;
         const int lane_off = (wave * TM * TN * 64 + lane) * 16;
         auto slot = [&](int sp) {
-            return __builtin_amdgcn_make_buffer_rsrc(partials + ((int64_t)t * SPLIT + sp) * kSlotBytes, (short)0,
+            return __builtin_amdgcn_make_buffer_rsrc(partials + ((int64_t)(t - full) * nsp + sp) * kSlotBytes, (short)0,
                                                      kSlotBytes, kBufferWord3);
         };
         const __amdgpu_buffer_rsrc_t mine = slot(split);
@@ -368,11 +386,11 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         if (tid == 0)
-            arrived = __hip_atomic_fetch_add(arrivals + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            arrived = __hip_atomic_fetch_add(arrivals + (t - full), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
-        if (arrived != SPLIT - 1)
+        if (arrived != (unsigned)(nsp - 1))
             return;
-        for (int sp = 0; sp < SPLIT; ++sp) {
+        for (int sp = 0; sp < nsp; ++sp) {
             if (sp == split)
                 continue;
             const __amdgpu_buffer_rsrc_t other = slot(sp);
@@ -383,7 +401,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
                     acc[a][i] += __builtin_amdgcn_raw_buffer_load_b128(other, lane_off + (a * TN + i) * 1024, 0, kSc1);
         }
         if (tid == 0)
-            arrivals[t] = 0u;
+            arrivals[t - full] = 0u;
     }
 
     // Epilogue: each wave passes its 64 x 64 accumulator tile through a private LDS
@@ -455,56 +473,74 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int WPE, int SPLIT>
+template <int BM, int BN, int WM, int WN, int NS, int WPE, bool SPLITK>
 hipError_t launch_t(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq, const float *sx,
                     const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, char *partials,
-                    unsigned *arrivals, hipStream_t s)
+                    unsigned *arrivals, int64_t full, int nsplit, hipStream_t s)
 {
     using C = GemmCfg<BM, BN, WM, WN, NS>;
     const int KC = (int)((K + 63) / 64);
     const int NBLK = (int)((N + 63) / 64);
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
-    const int items = tiles_m * tiles_n * SPLIT;
-    const int per_xcd = ((items + kXcds - 1) / kXcds + SPLIT - 1) / SPLIT * SPLIT;
+    const int64_t total = (int64_t)tiles_m * tiles_n;
+    const int full_x = (int)((full + kXcds - 1) / kXcds);
+    const int split_x = (int)((total - full + kXcds - 1) / kXcds);
+    const int64_t grid = (int64_t)kXcds * (full_x + (int64_t)split_x * nsplit);
     // 16-byte output stores need every row start 16-byte aligned.
     const int vec = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(acc) % 16 == 0);
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, WPE, SPLIT>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0,
-                       s, Wp, w_scale, Xq, ldq, sx, xsum, M, N, KC, NBLK, tiles_m, tiles_n, kGroup, Y, acc,
-                       vec | (row_scales ? 2 : 0),
-                       partials, arrivals, per_xcd);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, NS, WPE, SPLITK>), dim3((unsigned)grid), dim3(C::kThreads), 0, s, Wp,
+                       w_scale, Xq, ldq, sx, xsum, M, N, KC, NBLK, tiles_m, tiles_n, kGroup, Y, acc,
+                       vec | (row_scales ? 2 : 0), partials, arrivals, (int)full, nsplit, full_x, split_x);
     return hipGetLastError();
 }
 
 constexpr int kBM = 64, kBN = 256;
-
-int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
+constexpr int64_t kCUs = 256;
 
 }  // namespace
 
-// Workgroups per output tile (each over a contiguous share of the k-steps). Measured on
-// the 2B-class prefill shapes: splitting pays when the tiles alone leave most of the
-// 768 workgroup slots (three per CU) empty and every split keeps enough steps to amortize
-// its prologue, epilogue and the partial-tile hand-off through memory.
-int gemm_splits(int64_t M, int64_t N, int64_t K)
+int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
+
+// How a shape's tiles are spread over workgroups: the first `full` tiles whole, each later
+// one split over `nsplit` workgroups, each over a contiguous share of its k-steps.
+// Measured on the 2B-class prefill shapes at M = 256 to 4096:
+//  * Tail split: when the tiles fill whole rounds of one per CU and leave a last round of at
+//    most half the CUs, that round's tiles split up to one share per CU, every share keeping
+//    at least kMinTailSteps steps. A CU runs about one tile per period whatever else it
+//    holds, so without it the last round's CUs finish a whole tile after the rest. The
+//    K = 6912 shapes gain (320 tiles: 43.5 -> 38.8 us; 640: 66.8 -> 58.7 us); at K = 2560
+//    the 5-10 step shares cost what they save.
+//  * Otherwise every tile split in 2-4 (full = 0): it pays when the tiles alone leave most
+//    of the 768 workgroup slots (three per CU) empty and every split keeps enough steps to
+//    amortize its prologue, epilogue and the partial-tile hand-off through memory.
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K)
 {
     const int64_t tiles = gemm_tiles(M, N);
     const int64_t steps = ((K + 63) / 64 + 1) / 2;
+    const int64_t r = tiles % kCUs;
+    if (tiles >= kCUs && r > 0 && r <= kCUs / 2) {
+        int P = (int)std::min<int64_t>(4, kCUs / r);
+        while (P > 1 && steps < (int64_t)P * kMinTailSteps)
+            --P;
+        if (P > 1)
+            return {tiles - r, P};
+    }
     const int64_t min_steps = tiles <= 128 ? 6 : 13;
     for (int S = 4; S >= 2; --S)
         if (tiles * S <= 768 && steps >= S * min_steps)
-            return S;
-    return 1;
+            return {0, S};
+    return {tiles, 1};
 }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
-    const int S = gemm_splits(M, N, K);
-    if (S == 1)
+    const GemmPlan pl = gemm_plan(M, N, K);
+    if (pl.nsplit == 1)
         return 0;
-    const int64_t tiles = gemm_tiles(M, N);
-    return (size_t)(round_up(4 * tiles, 256) + tiles * S * (int64_t)kPartialBytes<kBM, kBN>);
+    const int64_t split_tiles = gemm_tiles(M, N) - pl.full;
+    return (size_t)(round_up(4 * split_tiles, 256) + split_tiles * pl.nsplit * (int64_t)kPartialBytes<kBM, kBN>);
 }
 
 hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq, const float *sx,
@@ -514,21 +550,24 @@ hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, bool row_scales, c
     // 64 x 256 blocks of 4 waves, three workgroups per CU (3-stage ring, 48 KB of LDS
     // each): with three waves per SIMD one wave's LDS reads, unpacking and barrier wait
     // hide under the others' MFMAs. Measured on the 2B-class prefill shapes against
-    // 128 x 256 blocks of 8 waves, 64 x 128 blocks of 2 waves and two workgroups per CU
-    // with a 4-stage ring.
-    const int S = gemm_splits(M, N, K);
+    // 128 x 256 blocks of 8 waves, 64 x 128 blocks of 2 waves, wave tiles of 32 and 128
+    // tokens and two workgroups per CU with a 4-stage ring.
+    const int64_t tiles = gemm_tiles(M, N);
+    const GemmPlan pl = gemm_plan(M, N, K);
     const size_t need = gemm_workspace_bytes(M, N, K);
-    if (S == 1 || !workspace || workspace_bytes < need)
-        return launch_t<kBM, kBN, 1, 4, 3, 3, 1>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, nullptr, nullptr, s);
+    if (pl.nsplit == 1 || !workspace || workspace_bytes < need)
+        return launch_t<kBM, kBN, 1, 4, 3, 3, false>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc,
+                                                     nullptr, nullptr, tiles, 1, s);
     unsigned *arrivals = static_cast<unsigned *>(workspace);
-    char *partials = static_cast<char *>(workspace) + round_up(4 * gemm_tiles(M, N), 256);
-    if (S == 2)
-        return launch_t<kBM, kBN, 1, 4, 3, 3, 2>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
-    if (S == 3)
-        return launch_t<kBM, kBN, 1, 4, 3, 3, 3>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
-    return launch_t<kBM, kBN, 1, 4, 3, 3, 4>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials, arrivals, s);
+    char *partials = static_cast<char *>(workspace) + round_up(4 * (tiles - pl.full), 256);
+    return launch_t<kBM, kBN, 1, 4, 3, 3, true>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, partials,
+                                                arrivals, pl.full, pl.nsplit, s);
 }
 
-int64_t gemm_arrival_words(int64_t M, int64_t N) { return gemm_tiles(M, N); }
+int64_t gemm_arrival_words(int64_t M, int64_t N, int64_t K)
+{
+    const GemmPlan pl = gemm_plan(M, N, K);
+    return pl.nsplit == 1 ? 0 : gemm_tiles(M, N) - pl.full;
+}
 
 }  // namespace bt

@@ -221,6 +221,18 @@ bt_status bt_ternary_gemm(const void *Wp, const float *w_scale, const int8_t *Xq
  * Errors are those of bt_ternary_gemm, plus BT_ERR_ALIGN for a misaligned workspace.
  */
 size_t bt_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+/*
+ * bt_gemm_split_plan -- how bt_ternary_gemm_ws spreads an M x N x K product over
+ * workgroups when given its workspace (host-only query, no device call). Output tiles are
+ * 64 tokens x 256 weight rows; the first *full_tiles of the library's tile order are
+ * computed whole and each later one is split over *splits workgroups (each over a
+ * contiguous share of K). *splits == 1: no split (bt_gemm_workspace_bytes is then 0);
+ * *full_tiles == 0 with *splits > 1: every tile is split. The workspace's leading
+ * (tiles - *full_tiles) 32-bit words are the arrival counters of the split tiles.
+ *   full_tiles, splits   host pointers, written on BT_OK.
+ * Errors: BT_ERR_NULL, BT_ERR_SHAPE (negative or oversized M, N or K).
+ */
+bt_status bt_gemm_split_plan(int64_t M, int64_t N, int64_t K, int64_t *full_tiles, int32_t *splits);
 bt_status bt_ternary_gemm_ws(const void *Wp, const float *w_scale, const int8_t *Xq,
                              const float *x_scale, const int32_t *x_sum, int64_t M, int64_t N,
                              int64_t K, float *Y, int32_t *acc, void *workspace,

@@ -54,6 +54,41 @@ def test_sizes():
     assert L.bt_pack_workspace_bytes(100, 5) == 1024
 
 
+def test_gemm_split_plan():
+    """The GEMM's work split (host logic): whole tiles, tail split, split of every tile, and
+    the workspace bytes that follow from it."""
+    def plan(M, N, K):
+        full, splits = ctypes.c_int64(-1), ctypes.c_int32(-1)
+        assert bt.lib().bt_gemm_split_plan(M, N, K, ctypes.byref(full), ctypes.byref(splits)) == BT_OK
+        return full.value, splits.value
+
+    def ws_bytes(M, N, full, splits):
+        tiles = -(-M // 64) * -(-N // 256)
+        if splits == 1:
+            return 0
+        n = tiles - full
+        return -(-4 * n // 256) * 256 + n * splits * 64 * 256 * 4
+
+    cases = {
+        # 2B prefill at M = 2048: 480, 320 and 1728 tiles of 20 steps stay whole; down
+        # (320 tiles of 54 steps) computes 256 whole and splits the last 64 in four.
+        (2048, 3840, 2560): (480, 1), (2048, 2560, 2560): (320, 1), (2048, 13824, 2560): (1728, 1),
+        (2048, 2560, 6912): (256, 4),
+        (4096, 2560, 6912): (512, 2),   # 640 tiles: the last 128 in two
+        (1024, 13824, 2560): (864, 1),  # tail of 96 tiles, but shares of 10 steps: whole
+        (256, 3840, 2560): (0, 3), (256, 2560, 6912): (0, 4), (100, 2500, 6900): (0, 4),
+        (70, 600, 2500): (0, 3), (65, 300, 1600): (0, 2),
+        (1100, 4096, 6200): (256, 4), (250, 22700, 3100): (256, 2),
+        (5, 5, 0): (1, 1), (0, 5, 5): (0, 1),
+    }
+    for (M, N, K), want in cases.items():
+        assert plan(M, N, K) == want, (M, N, K)
+        assert bt.lib().bt_gemm_workspace_bytes(M, N, K) == ws_bytes(M, N, *want), (M, N, K)
+    full, splits = ctypes.c_int64(), ctypes.c_int32()
+    assert bt.lib().bt_gemm_split_plan(-1, 5, 5, ctypes.byref(full), ctypes.byref(splits)) == BT_ERR_SHAPE
+    assert bt.lib().bt_gemm_split_plan(5, 5, 5, None, ctypes.byref(splits)) == BT_ERR_NULL
+
+
 def _gemv(L, *, Wp=FAKE, ws=FAKE, Xq=FAKE, sx=FAKE, xsum=FAKE, M=1, N=64, K=64, Y=FAKE, acc=0, algo=0):
     return L.bt_ternary_gemv_algo(Wp, ws, Xq, sx, xsum, M, N, K, Y, acc, algo, None)
 

@@ -255,30 +255,27 @@ def test_100b_down_decode_m16():
 
 
 # Split-K route (bt_ternary_gemm_ws): shapes chosen so that the split heuristic picks
-# 4, 3 and 2 workgroups per tile, ragged in M, N and K.
+# 4, 3 and 2 workgroups for every tile, ragged in M, N and K.
 SPLIT_SHAPES = [(100, 2500, 6900, 4), (70, 600, 2500, 3), (65, 300, 1600, 2)]
 
 
 def split_of(M, N, K):
-    """Workgroups per tile the library picks, read back from the workspace size."""
-    n = bt.gemm_workspace_bytes(M, N, K)
-    if n == 0:
-        return 1
-    tiles = -(-M // 64) * -(-N // 256)
-    counters = -(-4 * tiles // 256) * 256
-    assert (n - counters) % (tiles * 64 * 256 * 4) == 0
-    return (n - counters) // (tiles * 64 * 256 * 4)
+    """Workgroups per split tile the library picks (1: no split)."""
+    return bt.gemm_split_plan(M, N, K)[1]
 
 
-def counters_zero(ws, M, N):
+def counters_zero(ws, M, N, K):
+    """The arrival counters of the split tiles (the workspace's leading words) are zero."""
+    full, splits = bt.gemm_split_plan(M, N, K)
     tiles = -(-M // 64) * -(-N // 256)
-    return bool((ws[: 4 * tiles].view(torch.int32) == 0).all())
+    n = tiles - full if splits > 1 else 0
+    return bool((ws[: 4 * n].view(torch.int32) == 0).all())
 
 
 @pytest.mark.parametrize("M,N,K,S", SPLIT_SHAPES)
 def test_gemm_split_k(M, N, K, S):
     note(f"gemm split-K M={M} N={N} K={K} S={S}")
-    assert split_of(M, N, K) == S
+    assert bt.gemm_split_plan(M, N, K) == (0, S)
     W = synth.gaussian((N, K), 9150 + N, 0.02)
     X = synth.gaussian((M, K), 9650 + M)
     ref = oracle_layer(W, X)
@@ -286,12 +283,43 @@ def test_gemm_split_k(M, N, K, S):
     ws = bt.gemm_workspace(M, N, K, DEV)
     for _ in range(2):  # the second call relies on the first leaving the counters at zero
         check_product(pw, q, ref, M, N, bt.ternary_gemm, workspace=ws)
-        assert counters_zero(ws, M, N)
+        assert counters_zero(ws, M, N, K)
     # bit-identical to the unsplit route
     Y1, a1 = bt.ternary_gemm(pw, q, want_acc=True)
     Y2, a2 = bt.ternary_gemm(pw, q, want_acc=True, workspace=ws)
     np.testing.assert_array_equal(a1.cpu().numpy(), a2.cpu().numpy())
     np.testing.assert_array_equal(f32_bits(Y1.cpu().numpy()), f32_bits(Y2.cpu().numpy()))
+
+
+# Tail split: whole tiles for full rounds of one tile per CU, the last partial round's
+# tiles split (ragged in M, N and K): 288 tiles -> 256 whole + 32 in 4; 356 tiles ->
+# 256 whole + 100 in 2.
+TAIL_SHAPES = [(1100, 4096, 6200, 256, 4), (250, 22700, 3100, 256, 2)]
+
+
+@pytest.mark.parametrize("M,N,K,full,S", TAIL_SHAPES)
+def test_gemm_tail_split(M, N, K, full, S):
+    note(f"gemm tail split M={M} N={N} K={K}")
+    assert bt.gemm_split_plan(M, N, K) == (full, S)
+    W = synth.gaussian((N, K), 9160 + N, 0.02)
+    X = synth.gaussian((M, K), 9660 + M)
+    g = oracle.absmean(W)
+    T = oracle.ternarize(W, g)
+    Q, s, qs = oracle.quant_act(X)
+    # sampled token rows in every 64-token tile row, the last one included
+    rows = np.concatenate([np.arange(5, M, 61), [M - 1]])
+    acc_ref = oracle.ternary_matmul(T, Q[rows])
+    pw, q = gpu_pack(W), gpu_quant(X)
+    ws = bt.gemm_workspace(M, N, K, DEV)
+    for _ in range(2):  # the second call relies on the first leaving the counters at zero
+        Y, acc = bt.ternary_gemm(pw, q, want_acc=True, workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy()[rows], acc_ref)
+        assert tol_ok(Y.cpu().numpy()[rows], oracle.scale_epilogue(acc_ref, g, s[rows]))
+        assert counters_zero(ws, M, N, K)
+    Y1, a1 = bt.ternary_gemm(pw, q, want_acc=True)
+    np.testing.assert_array_equal(a1.cpu().numpy(), acc.cpu().numpy())
+    np.testing.assert_array_equal(f32_bits(Y1.cpu().numpy()), f32_bits(Y.cpu().numpy()))
 
 
 def test_gemm_split_k_small_workspace_falls_back():
@@ -331,7 +359,7 @@ def test_2b_prefill_split_shapes(M, j):
     Y1, a1 = bt.ternary_gemm(pw, q, want_acc=True)
     np.testing.assert_array_equal(a1.cpu().numpy(), acc.cpu().numpy())
     np.testing.assert_array_equal(f32_bits(Y1.cpu().numpy()), f32_bits(Y.cpu().numpy()))
-    assert counters_zero(ws, M, N)
+    assert counters_zero(ws, M, N, K)
 
 
 def test_2b_prefill_m2048_gate_up_sampled():
@@ -476,6 +504,32 @@ def test_linear_workspace_routes(M, N, K):
     Y, acc = bt.linear(to_dev(X), gpu_pack(W), want_acc=True)
     np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
     assert tol_ok(Y.cpu().numpy(), ref["Y"])
+
+
+def test_linear_tail_split_garbage_workspace():
+    """bt_ternary_linear on a shape whose GEMM splits only its last tiles, with a workspace
+    full of garbage: sampled rows against the oracle, all outputs bit-identical to the
+    unsplit product."""
+    M, N, K = 1100, 4096, 6200
+    note(f"linear tail split garbage workspace M={M} N={N} K={K}")
+    assert bt.gemm_split_plan(M, N, K) == (256, 4)
+    W = synth.gaussian((N, K), 9153, 0.02)
+    X = synth.gaussian((M, K), 9653)
+    g = oracle.absmean(W)
+    T = oracle.ternarize(W, g)
+    Q, s, qs = oracle.quant_act(X)
+    rows = np.concatenate([np.arange(7, M, 67), [M - 1]])
+    acc_ref = oracle.ternary_matmul(T, Q[rows])
+    pw = gpu_pack(W)
+    ws = torch.full((bt.linear_workspace_bytes(M, N, K),), 0xFF, dtype=torch.uint8, device=DEV)
+    for _ in range(2):
+        Y, acc = bt.linear(to_dev(X), pw, want_acc=True, workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy()[rows], acc_ref)
+        assert tol_ok(Y.cpu().numpy()[rows], oracle.scale_epilogue(acc_ref, g, s[rows]))
+    Y1, a1 = bt.ternary_gemm(pw, gpu_quant(X), want_acc=True)
+    np.testing.assert_array_equal(a1.cpu().numpy(), acc.cpu().numpy())
+    np.testing.assert_array_equal(f32_bits(Y1.cpu().numpy()), f32_bits(Y.cpu().numpy()))
 
 
 def test_linear_split_k_garbage_workspace():
