@@ -42,6 +42,18 @@ bt_status check_k(int64_t K)
     return BT_OK;
 }
 
+// Weight-matrix shapes: N rows of K, at most BT_MAX_MN elements.
+bt_status check_nk(int64_t N, int64_t K)
+{
+    if (N < 0 || N > BT_MAX_DIM)
+        return fail(BT_ERR_SHAPE, "N = %lld outside [0, 2^23]", (long long)N);
+    if (bt_status s = check_k(K))
+        return s;
+    if (N * K > BT_MAX_MN)
+        return fail(BT_ERR_SHAPE, "N * K = %lld above 2^36", (long long)(N * K));
+    return BT_OK;
+}
+
 // Common validation of the GEMV / GEMM arguments.
 bt_status check_product(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
                         const int32_t *x_sum, int64_t M, int64_t N, int64_t K, const float *Y, const int32_t *acc)
@@ -50,8 +62,10 @@ bt_status check_product(const void *Wp, const float *w_scale, const int8_t *Xq, 
         return fail(BT_ERR_SHAPE, "negative shape M = %lld, N = %lld", (long long)M, (long long)N);
     if (bt_status s = check_k(K))
         return s;
-    if (N > (int64_t)1 << 30 || M > (int64_t)1 << 30)
-        return fail(BT_ERR_SHAPE, "M = %lld or N = %lld above 2^30", (long long)M, (long long)N);
+    if (N > BT_MAX_DIM || M > BT_MAX_DIM)
+        return fail(BT_ERR_SHAPE, "M = %lld or N = %lld above 2^23", (long long)M, (long long)N);
+    if (M * N > BT_MAX_MN)
+        return fail(BT_ERR_SHAPE, "M * N = %lld above 2^36", (long long)(M * N));
     if (!Y && !acc)
         return fail(BT_ERR_NULL, "Y and acc are both NULL");
     if (M == 0 || N == 0)
@@ -90,9 +104,7 @@ size_t bt_pack_workspace_bytes(int64_t N, int64_t K)
 bt_status bt_pack_weights(const float *W, int64_t N, int64_t K, void *Wp, float *w_scale, void *workspace,
                           void *stream)
 {
-    if (N < 0 || N > (int64_t)1 << 30)
-        return fail(BT_ERR_SHAPE, "N = %lld outside [0, 2^30]", (long long)N);
-    if (bt_status s = check_k(K))
+    if (bt_status s = check_nk(N, K))
         return s;
     if (!w_scale)
         return fail(BT_ERR_NULL, "w_scale is NULL");
@@ -115,9 +127,7 @@ bt_status bt_pack_weights(const float *W, int64_t N, int64_t K, void *Wp, float 
 bt_status bt_pack_weights_rows(const float *W, int64_t N, int64_t K, const int64_t *group_rows, int64_t ngroups,
                                void *Wp, float *row_scale, void *workspace, void *stream)
 {
-    if (N < 0 || N > (int64_t)1 << 30)
-        return fail(BT_ERR_SHAPE, "N = %lld outside [0, 2^30]", (long long)N);
-    if (bt_status s = check_k(K))
+    if (bt_status s = check_nk(N, K))
         return s;
     bt::RowGroups groups{};
     if (group_rows) {
@@ -154,9 +164,7 @@ bt_status bt_pack_weights_rows(const float *W, int64_t N, int64_t K, const int64
 
 bt_status bt_unpack_weights(const void *Wp, int64_t N, int64_t K, int8_t *T, void *stream)
 {
-    if (N < 0 || N > (int64_t)1 << 30)
-        return fail(BT_ERR_SHAPE, "N = %lld outside [0, 2^30]", (long long)N);
-    if (bt_status s = check_k(K))
+    if (bt_status s = check_nk(N, K))
         return s;
     if (N == 0 || K == 0)
         return ok();
@@ -171,8 +179,8 @@ bt_status bt_unpack_weights(const void *Wp, int64_t N, int64_t K, int8_t *T, voi
 bt_status bt_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale, int32_t *x_sum,
                        void *stream)
 {
-    if (M < 0 || M > (int64_t)1 << 30)
-        return fail(BT_ERR_SHAPE, "M = %lld outside [0, 2^30]", (long long)M);
+    if (M < 0 || M > BT_MAX_DIM)
+        return fail(BT_ERR_SHAPE, "M = %lld outside [0, 2^23]", (long long)M);
     if (bt_status s = check_k(K))
         return s;
     if (M == 0)
@@ -280,8 +288,10 @@ static size_t linear_quant_bytes(int64_t M, int64_t K)
 static bt_status linear_impl(const void *Wp, const float *w_scale, bool rows, const float *X, int64_t M, int64_t N,
                              int64_t K, float *Y, int32_t *acc, void *workspace, void *stream)
 {
-    if (M < 0 || N < 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30)
+    if (M < 0 || N < 0 || M > BT_MAX_DIM || N > BT_MAX_DIM)
         return fail(BT_ERR_SHAPE, "shape M = %lld, N = %lld out of range", (long long)M, (long long)N);
+    if (M * N > BT_MAX_MN)
+        return fail(BT_ERR_SHAPE, "M * N = %lld above 2^36", (long long)(M * N));
     if (bt_status s = check_k(K))
         return s;
     if (!Y && !acc)
@@ -345,7 +355,7 @@ bt_status bt_ternary_gemv_rs(const void *Wp, const float *row_scale, const int8_
 
 size_t bt_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
-    if (M <= 0 || N <= 0 || K <= 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > BT_MAX_K)
+    if (M <= 0 || N <= 0 || K <= 0 || M > BT_MAX_DIM || N > BT_MAX_DIM || K > BT_MAX_K)
         return 0;
     return bt::gemm_workspace_bytes(M, N, K);
 }
@@ -354,7 +364,7 @@ bt_status bt_gemm_split_plan(int64_t M, int64_t N, int64_t K, int64_t *full_tile
 {
     if (!full_tiles || !splits)
         return fail(BT_ERR_NULL, "full_tiles and splits must not be NULL");
-    if (M < 0 || N < 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30)
+    if (M < 0 || N < 0 || M > BT_MAX_DIM || N > BT_MAX_DIM)
         return fail(BT_ERR_SHAPE, "shape M = %lld, N = %lld out of range", (long long)M, (long long)N);
     if (bt_status s = check_k(K))
         return s;
@@ -422,9 +432,7 @@ int64_t bt_act_bits_row_bytes(int64_t K, int32_t layout)
 bt_status bt_pack_weights_binary(const float *W, int64_t N, int64_t K, void *Wb, float *w_scale, void *workspace,
                                  void *stream)
 {
-    if (N < 0 || N > (int64_t)1 << 30)
-        return fail(BT_ERR_SHAPE, "N = %lld outside [0, 2^30]", (long long)N);
-    if (bt_status s = check_k(K))
+    if (bt_status s = check_nk(N, K))
         return s;
     if (N == 0 || K == 0)
         return fail(BT_ERR_SHAPE, "binary packing needs N > 0 and K > 0");
@@ -440,8 +448,8 @@ bt_status bt_pack_weights_binary(const float *W, int64_t N, int64_t K, void *Wb,
 bt_status bt_binarize_act(const float *X, int64_t M, int64_t K, int32_t layout, uint32_t *Xb, float *x_scale,
                           void *stream)
 {
-    if (M < 0 || M > (int64_t)1 << 30)
-        return fail(BT_ERR_SHAPE, "M = %lld outside [0, 2^30]", (long long)M);
+    if (M < 0 || M > BT_MAX_DIM)
+        return fail(BT_ERR_SHAPE, "M = %lld outside [0, 2^23]", (long long)M);
     if (bt_status s = check_k(K))
         return s;
     if (layout != BT_BITS_PLAIN && layout != BT_BITS_CODES)
@@ -461,8 +469,8 @@ static bt_status check_bits_product(const void *Wq, const float *w_scale, const 
 {
     if (M < 1 || M > BT_GEMV_MAX_M)
         return fail(BT_ERR_UNSUPPORTED, "1-bit GEMVs take 1 <= M <= %d (got %lld)", BT_GEMV_MAX_M, (long long)M);
-    if (N < 1 || N > (int64_t)1 << 30)
-        return fail(BT_ERR_SHAPE, "N = %lld outside [1, 2^30]", (long long)N);
+    if (N < 1 || N > BT_MAX_DIM)
+        return fail(BT_ERR_SHAPE, "N = %lld outside [1, 2^23]", (long long)N);
     if (K < 1 || K > BT_MAX_K)
         return fail(BT_ERR_SHAPE, "K = %lld outside [1, %d]", (long long)K, BT_MAX_K);
     if (!Y && !acc)

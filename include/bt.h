@@ -20,7 +20,9 @@
  *  - Arguments are validated on the host before any HIP call; on failure nothing
  *    is enqueued and a non-zero bt_status is returned (bt_last_error() says why).
  *  - Matrices are row-major. M = tokens, N = output features (rows of W),
- *    K = input features. 0 <= M, N; 0 <= K <= BT_MAX_K. M == 0 or N == 0 is a no-op.
+ *    K = input features. 0 <= M, N <= BT_MAX_DIM; 0 <= K <= BT_MAX_K; products
+ *    also M * N <= BT_MAX_MN (every launch then stays within 2^32 work-items).
+ *    Larger shapes fail with BT_ERR_SHAPE. M == 0 or N == 0 is a no-op.
  *  - Non-finite inputs are outside the contract; the results are then unspecified
  *    (but the kernels still stay in bounds).
  *  - Calls on different streams may run concurrently; a call reads only its
@@ -53,6 +55,10 @@ typedef int32_t bt_status;
 
 /* K is bounded so that |acc| <= 127*K < 2^24: acc then converts to fp32 exactly. */
 #define BT_MAX_K 131072
+/* Largest M and N: 2^23 (8.4 M tokens or output features). */
+#define BT_MAX_DIM 8388608LL
+/* Largest M * N of a product: 2^36 (a 256 GiB fp32 output). */
+#define BT_MAX_MN 68719476736LL
 /* Largest token count the decode GEMV entry point accepts. */
 #define BT_GEMV_MAX_M 16
 /* Largest number of explicit row groups bt_pack_weights_rows takes. */

@@ -138,6 +138,28 @@ def test_pack_and_quant_validation():
     assert L.bt_quant_act(FAKE, 0, 4, 0, 0, 0, None) == BT_OK
 
 
+def test_shape_limits():
+    """M, N <= 2^23, N * K and M * N <= 2^36: larger shapes fail on the host (every launch
+    then fits 2^32 work-items)."""
+    L = bt.lib()
+    big, over = 1 << 23, (1 << 23) + 1
+    assert L.bt_quant_act(FAKE, over, 4, FAKE, FAKE, FAKE, None) == BT_ERR_SHAPE
+    assert L.bt_pack_weights(FAKE, over, 4, FAKE, FAKE, FAKE, None) == BT_ERR_SHAPE
+    assert L.bt_pack_weights(FAKE, big, 1 << 17, FAKE, FAKE, FAKE, None) == BT_ERR_SHAPE  # N * K = 2^40
+    assert L.bt_unpack_weights(FAKE, big, 1 << 17, FAKE, None) == BT_ERR_SHAPE
+    assert L.bt_pack_weights_binary(FAKE, big, 1 << 17, FAKE, FAKE, FAKE, None) == BT_ERR_SHAPE
+    assert _gemv(L, N=over) == BT_ERR_SHAPE
+    # M * N = 2^37 fails; 2^36 passes the shape checks (and then fails on the NULL acc/Y pair)
+    assert L.bt_ternary_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, big, 1 << 14, 64, FAKE, 0, None) == BT_ERR_SHAPE
+    assert L.bt_ternary_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, big, 1 << 13, 64, 0, 0, None) == BT_ERR_NULL
+    assert b"2^36" in _reason(L, lambda: L.bt_ternary_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, big, 1 << 14, 64, FAKE, 0,
+                                                           None))
+    assert L.bt_ternary_linear(FAKE, FAKE, FAKE, over, 64, 64, FAKE, 0, FAKE, None) == BT_ERR_SHAPE
+    # the linear layer refuses before its quantizer launch, so nothing is enqueued
+    assert L.bt_ternary_linear(FAKE, FAKE, FAKE, big, 1 << 14, 64, FAKE, 0, FAKE, None) == BT_ERR_SHAPE
+    assert L.bt_gemm_workspace_bytes(over, 64, 64) == 0
+
+
 def test_status_strings():
     L = bt.lib()
     names = [L.bt_status_str(i).decode() for i in range(6)]
