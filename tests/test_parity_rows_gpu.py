@@ -129,6 +129,31 @@ def test_gemm_rows_split_and_plain():
     assert tol_ok(Y1.cpu().numpy(), ref["Y"])
 
 
+def test_gemm_rows_tail_split():
+    """Row scales on the tail-split route (256 whole tiles, the last 32 split in four):
+    sampled rows against the oracle, every output bit-identical to the unsplit route."""
+    M, N, K, groups = 1100, 4096, 6200, [2048, 1024, 1024]
+    note(f"gemm_rs tail split M={M} N={N} K={K}")
+    assert bt.gemm_split_plan(M, N, K) == (256, 4)
+    W = grouped(N, K, groups, 8800)
+    X = synth.gaussian((M, K), 8801)
+    rs = oracle.absmean_rows(W, groups)
+    T = oracle.ternarize_rows(W, rs)
+    Q, s, qs = oracle.quant_act(X)
+    rows = np.concatenate([np.arange(3, M, 59), [M - 1]])
+    acc_ref = oracle.ternary_matmul(T, Q[rows])
+    pw = bt.pack_weights_rows(to_dev(W), groups)
+    q = bt.quant_act(to_dev(X))
+    ws = bt.gemm_workspace(M, N, K, DEV)
+    Y1, acc1 = bt.ternary_gemm(pw, q, want_acc=True)
+    Y2, acc2 = bt.ternary_gemm(pw, q, want_acc=True, workspace=ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc2.cpu().numpy()[rows], acc_ref)
+    np.testing.assert_array_equal(acc1.cpu().numpy(), acc2.cpu().numpy())
+    np.testing.assert_array_equal(Y1.cpu().numpy(), Y2.cpu().numpy())
+    assert tol_ok(Y2.cpu().numpy()[rows], oracle.scale_epilogue_rows(acc_ref, rs, s[rows]))
+
+
 def test_rows_group_errors():
     W = torch.zeros((10, 8), dtype=torch.float32, device=DEV)
     for bad in ([4, 5], [4, 7], [0, 10], [1] * 10):
