@@ -208,7 +208,7 @@ def run_gpu(args, spec):
     else:
         names = {"mfma": "k_gemv_direct", "staged": "k_gemv_staged", "dot4": "k_gemv_dot4", "lut": "k_gemv_lut"}
         if args.gemv_algo == "auto":  # the library's pick per shape (BT_GEMV_AUTO), as bt_ternary_linear makes it
-            picks = ["staged" if M >= 5 and M * ((K + 255) // 256 * 256) <= 131072 else "mfma" for _, _, K in shapes]
+            picks = ["staged" if M * ((K + 255) // 256 * 256) <= 131072 else "mfma" for _, _, K in shapes]
             kernel = " + ".join(dict.fromkeys(names[c] for c in picks))
         else:
             kernel = names[args.gemv_algo]

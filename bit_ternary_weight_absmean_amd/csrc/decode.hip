@@ -855,7 +855,7 @@ int pick_rb(int64_t N)
 }
 
 // Token capacity of the fused kernel (it takes M <= 4: past that one quantizer launch
-// and the direct kernel are faster).
+// and a pre-quantized GEMV are faster).
 int pick_mt(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
 
 // k-splits per 16-row block: enough waves to give every SIMD one (1024 waves), two for

@@ -65,13 +65,13 @@ typedef int32_t bt_status;
 #define BT_MAX_ROW_GROUPS 8
 
 /* Decode GEMV kernel choices for bt_ternary_gemv_algo. */
-#define BT_GEMV_AUTO 0 /* pick by M from the library's launch table             */
+#define BT_GEMV_AUTO 0 /* BT_GEMV_STAGED where it fits, else BT_GEMV_MFMA        */
 #define BT_GEMV_DOT4 1 /* one lane per weight row, v_dot4 with the x chunk in SGPRs */
 #define BT_GEMV_MFMA 2 /* int8 MFMA 16x16x64, 64 weight rows per wave             */
 #define BT_GEMV_STAGED 4 /* int8 MFMA with the int8 activations staged once per workgroup
                             in LDS: M <= 16 with M * (K rounded up to 256) <= 131072
-                            bytes, else BT_ERR_UNSUPPORTED (BT_GEMV_AUTO picks it from
-                            5 tokens on when it fits, BT_GEMV_MFMA otherwise) */
+                            bytes, else BT_ERR_UNSUPPORTED (BT_GEMV_AUTO picks it
+                            whenever it fits, BT_GEMV_MFMA otherwise) */
 #define BT_GEMV_LUT 3  /* table lookup (T-MAC / TL1 style): M == 1 only, and K small
                           enough for its LDS tables (16 bytes per k; the device's
                           per-workgroup LDS limit), else BT_ERR_UNSUPPORTED      */
