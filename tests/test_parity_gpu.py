@@ -630,7 +630,10 @@ def test_gemv_lut_row_scales_and_limits():
 STAGED_CASES = [(5, 100, 300), (8, 130, 129), (8, 4096, 4096), (12, 600, 2560), (16, 2560, 1000),
                 (16, 13824, 2560), (7, 20000, 520), (16, 65, 4096), (1, 3840, 2560), (4, 300, 517),
                 # four chunks per thread: above 64 KB of staged rows, up to the 128 KB limit
-                (16, 10240, 8192), (9, 300, 11008)]
+                (16, 10240, 8192), (9, 300, 11008),
+                # degenerate and maximum shapes: one column, one row, K = BT_MAX_K at one token,
+                # and 128 KB of staged rows at two tokens
+                (16, 70, 1), (16, 1, 300), (1, 70, 131072), (2, 33, 65536)]
 
 
 @pytest.mark.parametrize("M,N,K", STAGED_CASES)
