@@ -19,7 +19,9 @@
 //    1 KB block), through a ring of NS stages, with no register staging and no LDS
 //    store instructions. Each lane quad of a load reads one 64-byte segment (adjacent
 //    lanes, adjacent addresses): scattering a quad over rows measured 10% slower.
-//  * LDS layouts, read without bank conflicts:
+//  * LDS layouts (in the 4-byte bank model every 16-lane group of an operand read covers all
+//    64 banks; the hardware still counts ~1.45 conflict cycles per LDS read, as it does for
+//    any 16-lane read spread over 16 rows):
 //      activations: per 16-row tile, two 1 KB halves of 8 rows x 128 bytes; row rho of
 //                   half h keeps piece p in 16-byte slot p ^ rho ^ h;
 //      weights:     the packed layout itself, [64-row block][64-k chunk][row][16 bytes].
