@@ -96,6 +96,32 @@ def parse():
 
 
 # ----------------------------------------------------------------- workloads
+# Token counts each workload is measured at (``--m``). tests/test_plan_coverage.py checks that
+# every kernel instance these steps launch -- default, --split and --row-scales routes -- is
+# also run by a parity test against the oracle.
+WORKLOAD_M = {"2b_decode": (1,), "7b_decode": (1, 2, 4, 8), "100b_decode": (1, 2, 4, 16), "2b_prefill": (256, 2048)}
+
+
+def step_plans(spec, split=False, row_scales=False, gemv_algo="auto"):
+    """The kernel instances (bt_kernel_plan text) one step of ``spec`` launches, per matrix."""
+    import bit_ternary_weight_absmean_amd as bt
+
+    M = spec["M"]
+    algo = {"auto": bt.GEMV_AUTO, "mfma": bt.GEMV_MFMA, "staged": bt.GEMV_STAGED, "dot4": bt.GEMV_DOT4,
+            "lut": bt.GEMV_LUT}[gemv_algo]
+    plans = []
+    for _, N, K in spec["shapes"]:
+        if not split:
+            plans.append(bt.kernel_plan(bt.CALL_LINEAR, M, N, K, row_scales=row_scales))
+        elif spec["prefill"] or M > bt.GEMV_MAX_M:
+            plans.append(bt.kernel_plan(bt.CALL_QUANT, M, N, K) + " + " +
+                         bt.kernel_plan(bt.CALL_GEMM_WS, M, N, K, row_scales=row_scales))
+        else:
+            plans.append(bt.kernel_plan(bt.CALL_QUANT, M, N, K) + " + " +
+                         bt.kernel_plan(bt.CALL_GEMV, M, N, K, algo, row_scales=row_scales))
+    return plans
+
+
 def workload_spec(name, m):
     from bit_ternary_weight_absmean_amd import synth
 

@@ -13,6 +13,11 @@ from ._lib import BTError, lib
 from .api import (
     BITS_CODES,
     BITS_PLAIN,
+    CALL_GEMM,
+    CALL_GEMM_WS,
+    CALL_GEMV,
+    CALL_LINEAR,
+    CALL_QUANT,
     GEMV_AUTO,
     GEMV_DOT4,
     GEMV_LUT,
@@ -26,6 +31,7 @@ from .api import (
     gemm_split_plan,
     gemm_workspace,
     gemm_workspace_bytes,
+    kernel_plan,
     linear,
     linear_workspace_bytes,
     pack_weights,
@@ -44,5 +50,5 @@ __all__ = [
     "BITS_CODES", "BITS_PLAIN", "binarize_act", "binary_gemv", "pack_weights_binary", "ternary_gemv_a1",
     "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_LUT", "GEMV_MFMA", "GEMV_STAGED", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
     "gemm_split_plan", "gemm_workspace", "gemm_workspace_bytes", "linear", "linear_workspace_bytes", "pack_weights", "pack_weights_rows", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
-    "ternary_gemv", "unpack_weights",
+    "ternary_gemv", "unpack_weights", "kernel_plan", "CALL_LINEAR", "CALL_GEMV", "CALL_GEMM", "CALL_GEMM_WS", "CALL_QUANT",
 ]

@@ -35,6 +35,7 @@ SIGNATURES = {
     "bt_binarize_act": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "bt_binary_gemv": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "bt_ternary_gemv_a1": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "bt_kernel_plan": (_i32, [_i32, _i64, _i64, _i64, _i32, _i32, ctypes.c_char_p, _sz]),
     "bt_status_str": (ctypes.c_char_p, [_i32]),
     "bt_last_error": (ctypes.c_char_p, []),
 }

@@ -507,6 +507,72 @@ bt_status bt_ternary_gemv_a1(const void *Wp, const float *w_scale, const uint32_
                       "bt_ternary_gemv_a1 launch");
 }
 
+bt_status bt_kernel_plan(int32_t call, int64_t M, int64_t N, int64_t K, int32_t algo, int32_t row_scales, char *buf,
+                         size_t len)
+{
+    if (!buf || len == 0)
+        return fail(BT_ERR_NULL, "buf is NULL or len is 0");
+    buf[0] = '\0';
+    if (call < BT_CALL_LINEAR || call > BT_CALL_QUANT)
+        return fail(BT_ERR_UNSUPPORTED, "unknown call %d", (int)call);
+    if (M < 0 || N < 0 || M > BT_MAX_DIM || N > BT_MAX_DIM || M * N > BT_MAX_MN)
+        return fail(BT_ERR_SHAPE, "shape M = %lld, N = %lld out of range", (long long)M, (long long)N);
+    if (bt_status s = check_k(K))
+        return s;
+    const bool rows = row_scales != 0;
+    if (M == 0 || (N == 0 && call != BT_CALL_QUANT))
+        return ok();  // no launch
+    int used = 0;
+    auto room = [&]() { return len > (size_t)used ? len - (size_t)used : 0; };
+    auto add = [&](int n) { used += n > 0 ? n : 0; };
+    auto gemv_plan = [&](int32_t a) -> bt_status {
+        if (M > BT_GEMV_MAX_M)
+            return fail(BT_ERR_UNSUPPORTED, "gemv takes M <= %d", BT_GEMV_MAX_M);
+        if (a == BT_GEMV_AUTO)
+            a = bt::gemv_staged_fits(M, N, K) ? BT_GEMV_STAGED : BT_GEMV_MFMA;
+        if (a == BT_GEMV_STAGED && K == 0)
+            a = BT_GEMV_MFMA;
+        if (a == BT_GEMV_LUT && K == 0)
+            a = BT_GEMV_MFMA;
+        switch (a) {
+        case BT_GEMV_STAGED:
+            if (!bt::gemv_staged_fits(M, N, K))
+                return fail(BT_ERR_UNSUPPORTED, "staged gemv does not take this shape");
+            add(bt::plan_gemv_staged(M, N, K, rows, buf + used, room()));
+            return ok();
+        case BT_GEMV_MFMA: add(bt::plan_gemv_mfma(M, N, K, rows, buf + used, room())); return ok();
+        case BT_GEMV_DOT4:
+            if (M > 4)
+                return fail(BT_ERR_UNSUPPORTED, "dot4 gemv takes M <= 4");
+            add(snprintf(buf + used, room(), "k_gemv_dot4<MT=%d>(rows=%d)", (int)M, (int)rows));
+            return ok();
+        case BT_GEMV_LUT:
+            if (M != 1)
+                return fail(BT_ERR_UNSUPPORTED, "lut gemv takes M == 1");
+            add(snprintf(buf + used, room(), "k_gemv_lut(rows=%d)", (int)rows));
+            return ok();
+        default: return fail(BT_ERR_UNSUPPORTED, "unknown gemv algo %d", (int)a);
+        }
+    };
+    switch (call) {
+    case BT_CALL_GEMV: return gemv_plan(algo);
+    case BT_CALL_GEMM: add(bt::plan_gemm(M, N, K, rows, false, buf, len)); return ok();
+    case BT_CALL_GEMM_WS: add(bt::plan_gemm(M, N, K, rows, true, buf, len)); return ok();
+    case BT_CALL_QUANT: add(bt::plan_quant_act(M, K, buf, len)); return ok();
+    default: break;
+    }
+    if (linear_fused(M, N, K)) {
+        add(bt::plan_linear_decode(M, N, K, rows, buf, len));
+        return ok();
+    }
+    add(bt::plan_quant_act(M, K, buf, len));
+    add(snprintf(buf + used, room(), " + "));
+    if (M <= BT_GEMV_MAX_M)
+        return gemv_plan(BT_GEMV_AUTO);
+    add(bt::plan_gemm(M, N, K, rows, true, buf + used, room()));
+    return ok();
+}
+
 const char *bt_status_str(bt_status s)
 {
     switch (s) {

@@ -19,6 +19,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
 
 namespace bt {
 
@@ -103,5 +104,13 @@ int64_t gemm_arrival_words(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq,
                        const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
                        void *workspace, size_t workspace_bytes, hipStream_t s);
+
+// Names of the kernel instances the launchers pick for a call (host-only, snprintf
+// semantics; 16-byte aligned activation rows assumed), for bt_kernel_plan.
+int plan_quant_act(int64_t M, int64_t K, char *buf, size_t len);
+int plan_linear_decode(int64_t M, int64_t N, int64_t K, bool row_scales, char *buf, size_t len);
+int plan_gemv_staged(int64_t M, int64_t N, int64_t K, bool row_scales, char *buf, size_t len);
+int plan_gemv_mfma(int64_t M, int64_t N, int64_t K, bool row_scales, char *buf, size_t len);
+int plan_gemm(int64_t M, int64_t N, int64_t K, bool row_scales, bool split_workspace, char *buf, size_t len);
 
 }  // namespace bt

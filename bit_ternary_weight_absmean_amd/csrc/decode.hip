@@ -686,8 +686,9 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
 }
 
 // ------------------------------------------------------------- staged kernel
-// Pre-quantized activations for 5 <= M <= 16 tokens (bt_ternary_gemv, and the unfused
-// route of bt_ternary_linear): the fused kernel's streaming design -- eight waves, k-splits
+// Pre-quantized activations for 1 <= M <= 16 tokens whose int8 rows fit the LDS limit
+// below (BT_GEMV_AUTO takes it wherever they fit: bt_ternary_gemv, and the unfused route
+// of bt_ternary_linear): the fused kernel's streaming design -- eight waves, k-splits
 // S, two weight batches in flight, every MFMA B operand one 16-byte LDS read -- with its
 // quantizer replaced by a copy of the int8 rows (bt_act_row_bytes(K) bytes each, zero past
 // K) into the same transposed chunk layout. The activations then cross the L2 once per
@@ -873,6 +874,13 @@ int pick_s(int64_t N)
     return s;
 }
 
+// Batch size: the steps of 256 k a wave owns (at most ceil(steps / S)) over two batches.
+int pick_u(int64_t K, int s)
+{
+    const int64_t mine = ((K + 255) / 256 + s - 1) / s;
+    return mine <= 2 ? 1 : mine <= 4 ? 2 : mine <= 6 ? 3 : 4;
+}
+
 size_t fused_lds(int64_t M, int64_t K, int s, int rx)
 {
     const int64_t KC = (K + 63) / 64;
@@ -880,12 +888,14 @@ size_t fused_lds(int64_t M, int64_t K, int s, int rx)
     return 2 * kFusedWaves * kMaxM * 4 + (s > 1 ? kFusedWaves * 256 * 4 : 0) + (size_t)M * fused_pitch(KC4, rx);
 }
 
-// The register path's float4 per thread and token (0: streaming path), as launch_fused_t
-// picks it for 16-byte aligned activations; it sets the LDS row pitch.
-int fused_rx(int64_t M, int64_t K)
+// The register path's float4 per thread and token (0: streaming path): for rows that are
+// 16-byte aligned with K % 4 == 0 and whose share per thread fits kXRegs float4 over all
+// the kernel's tokens, the smallest power of two RX with RX * 512 >= K / 4. It also sets
+// the LDS row pitch.
+int fused_rx(int64_t M, int64_t K, bool aligned16)
 {
     const int64_t K4 = K / 4, T = kFusedWaves * 64;
-    if (K <= 0 || (K & 3) != 0)
+    if (K <= 0 || (K & 3) != 0 || !aligned16)
         return 0;
     int rx = 1;
     while ((int64_t)rx * T < K4)
@@ -893,9 +903,20 @@ int fused_rx(int64_t M, int64_t K)
     return rx * pick_mt(M) > kXRegs ? 0 : rx;
 }
 
+// Template arguments of the fused kernel for one call (k_linear_decode<MT, S, RX, U>).
+struct FusedPick {
+    int mt, s, rx, u;
+};
+
+FusedPick pick_fused(int64_t M, int64_t N, int64_t K, bool aligned16)
+{
+    const int s = pick_s(N);
+    return {pick_mt(M), s, fused_rx(M, K, aligned16), pick_u(K, s)};
+}
+
 template <int MT, int S, int RX, int U>
-hipError_t launch_fused_u(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M, int64_t N, int64_t K,
-                          float *Y, int32_t *acc, hipStream_t s)
+hipError_t launch_fused_u(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M, int64_t N,
+                          int64_t K, float *Y, int32_t *acc, hipStream_t s)
 {
     constexpr int RBW = kFusedWaves / S;
     const int64_t nb16 = (N + 15) / 16;
@@ -909,54 +930,43 @@ hipError_t launch_fused_u(const uint4 *Wp, const float *w_scale, bool row_scales
     return hipGetLastError();
 }
 
-// Batch size: the steps of 256 k a wave owns (at most ceil(steps / S)) over two batches.
 template <int MT, int S, int RX>
-hipError_t launch_fused_rx(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M, int64_t N, int64_t K,
-                           float *Y, int32_t *acc, hipStream_t s)
+hipError_t launch_fused_rx(const FusedPick &p, const uint4 *Wp, const float *w_scale, bool row_scales, const float *X,
+                           int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
 {
-    const int64_t steps = (K + 255) / 256;
-    const int64_t mine = (steps + S - 1) / S;
-    if (mine <= 2)
-        return launch_fused_u<MT, S, RX, 1>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    if (mine <= 4)
-        return launch_fused_u<MT, S, RX, 2>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    if (mine <= 6)
-        return launch_fused_u<MT, S, RX, 3>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    return launch_fused_u<MT, S, RX, 4>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    switch (p.u) {
+    case 1: return launch_fused_u<MT, S, RX, 1>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 2: return launch_fused_u<MT, S, RX, 2>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 3: return launch_fused_u<MT, S, RX, 3>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    default: return launch_fused_u<MT, S, RX, 4>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    }
 }
 
-// Register path when the rows are 16-byte aligned with K % 4 == 0 and each thread's
-// share fits kXRegs float4 over all MT tokens: RX = the smallest power of two with
-// RX * 512 >= K / 4.
+// RX * MT <= kXRegs holds for every pick (fused_rx), so the clamps below only keep
+// combinations that are never launched from being instantiated.
 template <int MT, int S>
-hipError_t launch_fused_t(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M, int64_t N, int64_t K,
-                          float *Y, int32_t *acc, hipStream_t s)
+hipError_t launch_fused_t(const FusedPick &p, const uint4 *Wp, const float *w_scale, bool row_scales, const float *X,
+                          int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
 {
-    const int64_t K4 = K / 4, T = kFusedWaves * 64;
-    const bool vec = K > 0 && (K & 3) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
-    int rx = 1;
-    while ((int64_t)rx * T < K4)
-        rx *= 2;
-    if (!vec || rx * MT > kXRegs)
-        return launch_fused_rx<MT, S, 0>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    switch (rx) {
-    case 1: return launch_fused_rx<MT, S, 1>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    case 2: return launch_fused_rx<MT, S, (MT <= 8 ? 2 : 1)>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    case 4: return launch_fused_rx<MT, S, (MT <= 4 ? 4 : 1)>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    case 8: return launch_fused_rx<MT, S, (MT <= 2 ? 8 : 1)>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    default: return launch_fused_rx<MT, S, (MT <= 1 ? 16 : 1)>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    switch (p.rx) {
+    case 0: return launch_fused_rx<MT, S, 0>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 1: return launch_fused_rx<MT, S, 1>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 2: return launch_fused_rx<MT, S, (MT <= 8 ? 2 : 1)>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 4: return launch_fused_rx<MT, S, (MT <= 4 ? 4 : 1)>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 8: return launch_fused_rx<MT, S, (MT <= 2 ? 8 : 1)>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    default: return launch_fused_rx<MT, S, (MT <= 1 ? 16 : 1)>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
     }
 }
 
 template <int MT>
-hipError_t launch_fused_mt(const uint4 *Wp, const float *w_scale, bool row_scales, const float *X, int64_t M, int64_t N, int64_t K,
-                           float *Y, int32_t *acc, hipStream_t s)
+hipError_t launch_fused_mt(const FusedPick &p, const uint4 *Wp, const float *w_scale, bool row_scales, const float *X,
+                           int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
 {
-    switch (pick_s(N)) {
-    case 1: return launch_fused_t<MT, 1>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    case 2: return launch_fused_t<MT, 2>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    case 4: return launch_fused_t<MT, 4>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    default: return launch_fused_t<MT, 8>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    switch (p.s) {
+    case 1: return launch_fused_t<MT, 1>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 2: return launch_fused_t<MT, 2>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 4: return launch_fused_t<MT, 4>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    default: return launch_fused_t<MT, 8>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
     }
 }
 
@@ -964,6 +974,20 @@ size_t staged_lds(int64_t M, int64_t K, int s)
 {
     const int KC4 = (int)(((K + 63) / 64 + 3) / 4 * 4);
     return (s > 1 ? kFusedWaves * 64 * 16 : 0) + (size_t)M * fused_pitch(KC4, 0);
+}
+
+// Template arguments of the staged kernel for one call (k_gemv_staged<MT, S, U, CH>): token
+// capacity 8 or 16, the fused kernel's k-splits and batch size, and the staged rows' 64-byte
+// chunks over the workgroup's threads (CH = 2 up to 64 KB, 4 up to 128 KB).
+struct StagedPick {
+    int mt, s, u, ch;
+};
+
+StagedPick pick_staged(int64_t M, int64_t N, int64_t K)
+{
+    const int s = pick_s(N);
+    const int64_t nchunks = M * (((K + 63) / 64 + 3) / 4 * 4);
+    return {M <= 8 ? 8 : 16, s, pick_u(K, s), nchunks <= 2 * kFusedWaves * 64 ? 2 : 4};
 }
 
 template <int MT, int S, int U, int CH>
@@ -982,59 +1006,70 @@ hipError_t launch_staged_ch(const uint4 *Wp, const float *w_scale, bool row_scal
     return hipGetLastError();
 }
 
-// Chunks per thread: the staged rows' 64-byte chunks over the workgroup's threads.
 template <int MT, int S, int U>
-hipError_t launch_staged_u(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, const float *sx,
-                           const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
+hipError_t launch_staged_u(const StagedPick &p, const uint4 *Wp, const float *w_scale, bool row_scales,
+                           const int8_t *Xq, const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K,
+                           float *Y, int32_t *acc, hipStream_t s)
 {
-    const int64_t nchunks = M * (((K + 63) / 64 + 3) / 4 * 4);
-    if (nchunks <= 2 * kFusedWaves * 64)
+    if (p.ch == 2)
         return launch_staged_ch<MT, S, U, 2>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
     return launch_staged_ch<MT, S, U, 4>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
 }
 
 template <int MT, int S>
-hipError_t launch_staged_s(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, const float *sx,
-                           const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
+hipError_t launch_staged_s(const StagedPick &p, const uint4 *Wp, const float *w_scale, bool row_scales,
+                           const int8_t *Xq, const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K,
+                           float *Y, int32_t *acc, hipStream_t s)
 {
-    const int64_t mine = ((K + 255) / 256 + S - 1) / S;
-    if (mine <= 2)
-        return launch_staged_u<MT, S, 1>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
-    if (mine <= 4)
-        return launch_staged_u<MT, S, 2>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
-    if (mine <= 6)
-        return launch_staged_u<MT, S, 3>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
-    return launch_staged_u<MT, S, 4>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
-}
-
-template <int MT>
-hipError_t launch_staged_mt(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, const float *sx,
-                            const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t s)
-{
-    switch (pick_s(N)) {
-    case 1: return launch_staged_s<MT, 1>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
-    case 2: return launch_staged_s<MT, 2>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
-    case 4: return launch_staged_s<MT, 4>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
-    default: return launch_staged_s<MT, 8>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    switch (p.u) {
+    case 1: return launch_staged_u<MT, S, 1>(p, Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    case 2: return launch_staged_u<MT, S, 2>(p, Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    case 3: return launch_staged_u<MT, S, 3>(p, Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    default: return launch_staged_u<MT, S, 4>(p, Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
     }
 }
 
+template <int MT>
+hipError_t launch_staged_mt(const StagedPick &p, const uint4 *Wp, const float *w_scale, bool row_scales,
+                            const int8_t *Xq, const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K,
+                            float *Y, int32_t *acc, hipStream_t s)
+{
+    switch (p.s) {
+    case 1: return launch_staged_s<MT, 1>(p, Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    case 2: return launch_staged_s<MT, 2>(p, Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    case 4: return launch_staged_s<MT, 4>(p, Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    default: return launch_staged_s<MT, 8>(p, Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    }
+}
+
+// The direct kernel for one call: RB row blocks per workgroup, and for one row block the
+// double-buffered form with batches of U steps. One row block: two-step batches, two in
+// flight once a wave owns more than two steps. More row blocks: the single-batch kernel
+// (measured faster there: more waves resident).
+struct DirectPick {
+    int rb, u;  // u == 0: k_gemv_direct<RB>; else k_gemv_direct_db<RB, u>
+};
+
+DirectPick pick_direct(int64_t N, int64_t K)
+{
+    const int rb = pick_rb(N);
+    const int64_t mine = ((K + 255) / 256 + kDirectWaves - 1) / kDirectWaves;
+    return {rb, rb > 1 ? 0 : mine <= 2 ? 1 : 2};
+}
+
 template <int RB>
-hipError_t launch_direct_t(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq, const float *sx,
-                           const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
-                           hipStream_t s)
+hipError_t launch_direct_t(const DirectPick &p, const uint4 *Wp, const float *w_scale, bool row_scales,
+                           const int8_t *Xq, int64_t ldq, const float *sx, const int32_t *xsum, int64_t M, int64_t N,
+                           int64_t K, float *Y, int32_t *acc, hipStream_t s)
 {
     const int KC = (int)((K + 63) / 64);
     const int NB16 = (int)(((N + 63) / 64) * 4);
     const int64_t nb16 = (N + 15) / 16;
     const dim3 grid((unsigned)((nb16 + RB - 1) / RB)), block(kDirectWaves * 64);
-    // One row block: two-step batches, two in flight once a wave owns more than two steps.
-    // More row blocks: the single-batch kernel (measured faster there: more waves resident).
-    const int64_t mine = ((K + 255) / 256 + kDirectWaves - 1) / kDirectWaves;
-    if (RB > 1)
+    if (p.u == 0)
         hipLaunchKernelGGL((k_gemv_direct<RB>), grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M, N, KC, NB16, Y,
                            acc, (int)row_scales);
-    else if (mine <= 2)
+    else if (p.u == 1)
         hipLaunchKernelGGL((k_gemv_direct_db<RB, 1>), grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, (int)M,
                            N, KC, NB16, Y, acc, (int)row_scales);
     else
@@ -1046,7 +1081,10 @@ hipError_t launch_direct_t(const uint4 *Wp, const float *w_scale, bool row_scale
 }  // namespace
 
 // An upper bound for any activation alignment: the register path's pitch is the larger.
-size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K) { return fused_lds(M, K, pick_s(N), fused_rx(M, K)); }
+size_t decode_fused_lds_bytes(int64_t M, int64_t N, int64_t K)
+{
+    return fused_lds(M, K, pick_s(N), fused_rx(M, K, true));
+}
 
 // The staged kernel takes up to 16 tokens whose int8 rows fit kStagedLdsLimit bytes of LDS
 // (each thread then copies at most kStagedMaxChunks chunks; with the k-split area and the
@@ -1065,19 +1103,21 @@ hipError_t launch_gemv_staged(const uint4 *Wp, const float *w_scale, bool row_sc
 {
     if (!gemv_staged_fits(M, N, K))
         return hipErrorInvalidValue;
-    if (M <= 8)
-        return launch_staged_mt<8>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
-    return launch_staged_mt<16>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    const StagedPick p = pick_staged(M, N, K);
+    if (p.mt == 8)
+        return launch_staged_mt<8>(p, Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+    return launch_staged_mt<16>(p, Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
 }
 
 hipError_t launch_gemv_mfma(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq,
                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
                             int32_t *acc, hipStream_t s)
 {
-    switch (pick_rb(N)) {
-    case 4: return launch_direct_t<4>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
-    case 2: return launch_direct_t<2>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
-    default: return launch_direct_t<1>(Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    const DirectPick p = pick_direct(N, K);
+    switch (p.rb) {
+    case 4: return launch_direct_t<4>(p, Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    case 2: return launch_direct_t<2>(p, Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
+    default: return launch_direct_t<1>(p, Wp, w_scale, row_scales, Xq, ldq, sx, xsum, M, N, K, Y, acc, s);
     }
 }
 
@@ -1086,11 +1126,35 @@ hipError_t launch_linear_decode(const uint4 *Wp, const float *w_scale, bool row_
 {
     if (M > 4)
         return hipErrorInvalidValue;
-    switch (pick_mt(M)) {
-    case 1: return launch_fused_mt<1>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    case 2: return launch_fused_mt<2>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
-    default: return launch_fused_mt<4>(Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    const FusedPick p = pick_fused(M, N, K, (reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    switch (p.mt) {
+    case 1: return launch_fused_mt<1>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    case 2: return launch_fused_mt<2>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
+    default: return launch_fused_mt<4>(p, Wp, w_scale, row_scales, X, M, N, K, Y, acc, s);
     }
+}
+
+// Names of the kernel instances the launchers above pick (host-only; for bt_kernel_plan).
+int plan_linear_decode(int64_t M, int64_t N, int64_t K, bool row_scales, char *buf, size_t len)
+{
+    const FusedPick p = pick_fused(M, N, K, true);
+    return snprintf(buf, len, "k_linear_decode<MT=%d,S=%d,RX=%d,U=%d,ROWS=%d>", p.mt, p.s, p.rx, p.u,
+                    (int)row_scales);
+}
+
+int plan_gemv_staged(int64_t M, int64_t N, int64_t K, bool row_scales, char *buf, size_t len)
+{
+    const StagedPick p = pick_staged(M, N, K);
+    return snprintf(buf, len, "k_gemv_staged<MT=%d,S=%d,U=%d,ROWS=%d,CH=%d>", p.mt, p.s, p.u, (int)row_scales, p.ch);
+}
+
+int plan_gemv_mfma(int64_t M, int64_t N, int64_t K, bool row_scales, char *buf, size_t len)
+{
+    (void)M;
+    const DirectPick p = pick_direct(N, K);
+    if (p.u == 0)
+        return snprintf(buf, len, "k_gemv_direct<RB=%d>(rows=%d)", p.rb, (int)row_scales);
+    return snprintf(buf, len, "k_gemv_direct_db<RB=%d,U=%d>(rows=%d)", p.rb, p.u, (int)row_scales);
 }
 
 }  // namespace bt

@@ -566,6 +566,16 @@ hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, bool row_scales, c
                                                 arrivals, pl.full, pl.nsplit, s);
 }
 
+int plan_gemm(int64_t M, int64_t N, int64_t K, bool row_scales, bool split_workspace, char *buf, size_t len)
+{
+    const GemmPlan pl = gemm_plan(M, N, K);
+    const int64_t tiles = gemm_tiles(M, N);
+    if (!split_workspace || pl.nsplit == 1)
+        return snprintf(buf, len, "k_gemm<SPLITK=0,ROWS=%d>[tiles=%lld]", (int)row_scales, (long long)tiles);
+    return snprintf(buf, len, "k_gemm<SPLITK=1,ROWS=%d>[tiles=%lld,full=%lld,splits=%d]", (int)row_scales,
+                    (long long)tiles, (long long)pl.full, pl.nsplit);
+}
+
 int64_t gemm_arrival_words(int64_t M, int64_t N, int64_t K)
 {
     const GemmPlan pl = gemm_plan(M, N, K);

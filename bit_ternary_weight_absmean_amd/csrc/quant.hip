@@ -177,7 +177,26 @@ __global__ __launch_bounds__(kThreads) void k_quant_act_reg(const float *__restr
     }
 }
 
+// Register kernel's float4 per thread (k_quant_act_reg<C>), or 0 for the two-pass kernel.
+int quant_reg_chunks(int64_t K, bool aligned16)
+{
+    if (K <= 0 || (K % 4) != 0 || !aligned16)
+        return 0;
+    const int64_t per_thread = (K / 4 + kThreads - 1) / kThreads;  // float4 chunks per thread
+    for (int c = 1; c <= 32; c *= 2)
+        if (per_thread <= c)
+            return c;
+    return 0;
+}
+
 }  // namespace
+
+int plan_quant_act(int64_t M, int64_t K, char *buf, size_t len)
+{
+    (void)M;
+    const int c = quant_reg_chunks(K, true);
+    return c ? snprintf(buf, len, "k_quant_act_reg<C=%d>", c) : snprintf(buf, len, "k_quant_act");
+}
 
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int64_t ldq, int8_t *Xq, float *sx,
                             int32_t *xsum, unsigned *clear, int64_t clear_words, hipStream_t s)
@@ -185,8 +204,9 @@ hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int64_t ldq, i
     if (M <= 0)
         return hipGetLastError();
     const dim3 grid((unsigned)M), block(kThreads);
-    const bool reg = K > 0 && (K % 4) == 0 && (reinterpret_cast<uintptr_t>(X) % 16) == 0;
-    const int64_t per_thread = (K / 4 + kThreads - 1) / kThreads;  // float4 chunks per thread
+    const int c = quant_reg_chunks(K, (reinterpret_cast<uintptr_t>(X) % 16) == 0);
+    const bool reg = c > 0;
+    const int64_t per_thread = c;
     if (reg && per_thread <= 1)
         hipLaunchKernelGGL(k_quant_act_reg<1>, grid, block, 0, s, X, K, ldq, Xq, sx, xsum, clear, clear_words);
     else if (reg && per_thread <= 2)

@@ -340,6 +340,31 @@ bt_status bt_ternary_gemv_a1(const void *Wp, const float *w_scale, const uint32_
                              const float *x_scale, int64_t M, int64_t N, int64_t K, float *Y,
                              int32_t *acc, void *stream);
 
+/*
+ * bt_kernel_plan -- the kernel instances a call would launch, as text (a host-only query:
+ * no device call, nothing enqueued). For checking which specialisations a workload runs,
+ * e.g. that every one of them is covered by a test. The activation rows are taken to be
+ * 16-byte aligned (the fused and quantizer kernels pick their register path from that).
+ *   call        BT_CALL_LINEAR (bt_ternary_linear / _rs), BT_CALL_GEMV (bt_ternary_gemv_algo /
+ *               _rs with `algo`), BT_CALL_GEMM (bt_ternary_gemm, no workspace) or
+ *               BT_CALL_GEMM_WS (bt_ternary_gemm_ws / _rs with a workspace of
+ *               bt_gemm_workspace_bytes(M, N, K) bytes) or BT_CALL_QUANT (bt_quant_act).
+ *   M, N, K     the call's shape (N is ignored for BT_CALL_QUANT); algo is read for
+ *               BT_CALL_GEMV only; row_scales != 0 for the _rs entry points.
+ *   buf, len    host buffer receiving a NUL-terminated text (truncated to len - 1 bytes):
+ *               the kernels in launch order joined by " + ", each as name<template
+ *               arguments>; empty when the call launches nothing (M == 0 or N == 0).
+ * Errors: BT_ERR_NULL (buf), BT_ERR_SHAPE, BT_ERR_UNSUPPORTED -- those the call itself
+ * would return for the shape and kernel choice.
+ */
+#define BT_CALL_LINEAR 0
+#define BT_CALL_GEMV 1
+#define BT_CALL_GEMM 2
+#define BT_CALL_GEMM_WS 3
+#define BT_CALL_QUANT 4
+bt_status bt_kernel_plan(int32_t call, int64_t M, int64_t N, int64_t K, int32_t algo, int32_t row_scales,
+                         char *buf, size_t len);
+
 /* Static text for a status code. */
 const char *bt_status_str(bt_status s);
 
