@@ -24,6 +24,7 @@ from .api import (
     GEMV_MAX_M,
     GEMV_MFMA,
     GEMV_STAGED,
+    STATIC_SCRATCH_BYTES,
     PackedWeight,
     act_row_bytes,
     binarize_act,
@@ -33,6 +34,7 @@ from .api import (
     gemm_workspace_bytes,
     kernel_plan,
     linear,
+    linear_static,
     linear_workspace_bytes,
     pack_weights,
     pack_weights_binary,
@@ -50,5 +52,5 @@ __all__ = [
     "BITS_CODES", "BITS_PLAIN", "binarize_act", "binary_gemv", "pack_weights_binary", "ternary_gemv_a1",
     "BTError", "lib", "GEMV_AUTO", "GEMV_DOT4", "GEMV_LUT", "GEMV_MFMA", "GEMV_STAGED", "GEMV_MAX_M", "PackedWeight", "act_row_bytes",
     "gemm_split_plan", "gemm_workspace", "gemm_workspace_bytes", "linear", "linear_workspace_bytes", "pack_weights", "pack_weights_rows", "pack_workspace_bytes", "packed_weight_bytes", "quant_act", "ternary_gemm",
-    "ternary_gemv", "unpack_weights", "kernel_plan", "CALL_LINEAR", "CALL_GEMV", "CALL_GEMM", "CALL_GEMM_WS", "CALL_QUANT",
+    "ternary_gemv", "unpack_weights", "kernel_plan", "CALL_LINEAR", "CALL_GEMV", "CALL_GEMM", "CALL_GEMM_WS", "CALL_QUANT", "linear_static", "STATIC_SCRATCH_BYTES",
 ]

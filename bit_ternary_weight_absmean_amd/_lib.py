@@ -29,6 +29,7 @@ SIGNATURES = {
     "bt_ternary_gemv_rs": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _i32, _vp]),
     "bt_ternary_gemm_rs": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
     "bt_ternary_linear_rs": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "bt_ternary_linear_static": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "bt_binary_weight_bytes": (_sz, [_i64, _i64]),
     "bt_act_bits_row_bytes": (_i64, [_i64, _i32]),
     "bt_pack_weights_binary": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),

@@ -274,6 +274,29 @@ def linear(X: torch.Tensor, pw: PackedWeight, want_y=True, want_acc=False, out_y
     return Y, acc
 
 
+STATIC_SCRATCH_BYTES = 64 << 20  # BT_STATIC_SCRATCH_BYTES
+
+
+def linear_static(X: torch.Tensor, pw: PackedWeight, out_y=None, out_acc=None, want_y=True, want_acc=False):
+    """bt_ternary_linear_static: bt_ternary_linear without a workspace (the library's static
+    scratch serves the routes that need one). One scale per matrix only. Pass out_y / out_acc
+    to keep the call free of allocation."""
+    if pw.row_scales:
+        raise ValueError("bt_ternary_linear_static takes weights with one scale per matrix")
+    pw.check()
+    dev = pw.data.device
+    if X.dim() != 2:
+        raise ValueError(f"X must be [M, K], got shape {tuple(X.shape)}")
+    _need(X, "X", torch.float32, device=dev)
+    M, K = X.shape
+    if K != pw.K:
+        raise ValueError(f"X has K = {K}, weights have K = {pw.K}")
+    Y, acc = _outputs(M, pw.N, dev, want_y, want_acc, out_y, out_acc)
+    check(lib().bt_ternary_linear_static(_ptr(pw.data), _ptr(pw.scale), _ptr(X), M, pw.N, K, _ptr(Y), _ptr(acc),
+                                         _stream(dev)))
+    return Y, acc
+
+
 CALL_LINEAR, CALL_GEMV, CALL_GEMM, CALL_GEMM_WS, CALL_QUANT = 0, 1, 2, 3, 4
 
 

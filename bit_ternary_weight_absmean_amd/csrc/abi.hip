@@ -4,8 +4,16 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "bt.h"
 #include "bt_internal.h"
+
+// Scratch of bt_ternary_linear_static: one copy per GPU, held by the loaded library until
+// the process ends. Host code never passes `scratch` itself to a kernel (in host code the
+// name stands for a host-side shadow); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[BT_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -337,6 +345,47 @@ static bt_status linear_impl(const void *Wp, const float *w_scale, bool rows, co
     return gemm_impl(Wp, w_scale, rows, Xq, sx, xsum, M, N, K, Y, acc, gbytes ? gws : nullptr, gbytes, stream);
 }
 
+// Device address of `scratch` on the current device, looked up once per device.
+static bt_status static_scratch(void **out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex lock;
+    static void *addr[kMaxDevices];
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+        return fail(BT_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(BT_ERR_UNSUPPORTED, "device %d beyond the %d this library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> g(lock);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess || !p)
+            return fail(BT_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        e != hipSuccess ? hipGetErrorString(e) : "null address");
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return BT_OK;
+}
+
+static bt_status linear_static_impl(const void *Wp, const float *w_scale, bool rows, const float *X, int64_t M,
+                                    int64_t N, int64_t K, float *Y, int32_t *acc, void *stream)
+{
+    if (M < 0 || N < 0 || M > BT_MAX_DIM || N > BT_MAX_DIM || K < 0 || K > BT_MAX_K || M * N > BT_MAX_MN)
+        return linear_impl(Wp, w_scale, rows, X, M, N, K, Y, acc, nullptr, stream);  // its shape error
+    const size_t need = bt_linear_workspace_bytes(M, N, K);
+    if (need > (size_t)BT_STATIC_SCRATCH_BYTES)
+        return fail(BT_ERR_UNSUPPORTED,
+                    "M = %lld, N = %lld, K = %lld needs %zu bytes of scratch, above the static %lld bytes "
+                    "(use bt_ternary_linear with a workspace)",
+                    (long long)M, (long long)N, (long long)K, need, (long long)BT_STATIC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need > 0)
+        if (bt_status s = static_scratch(&ws))
+            return s;
+    return linear_impl(Wp, w_scale, rows, X, M, N, K, Y, acc, ws, stream);
+}
+
 bt_status bt_ternary_gemv_algo(const void *Wp, const float *w_scale, const int8_t *Xq, const float *x_scale,
                                const int32_t *x_sum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
                                int32_t algo, void *stream)
@@ -417,6 +466,12 @@ bt_status bt_ternary_linear_rs(const void *Wp, const float *row_scale, const flo
                                int64_t K, float *Y, int32_t *acc, void *workspace, void *stream)
 {
     return linear_impl(Wp, row_scale, true, X, M, N, K, Y, acc, workspace, stream);
+}
+
+bt_status bt_ternary_linear_static(const void *Wp, const float *w_scale, const float *X, int64_t M, int64_t N,
+                                   int64_t K, float *Y, int32_t *acc, void *stream)
+{
+    return linear_static_impl(Wp, w_scale, false, X, M, N, K, Y, acc, stream);
 }
 
 size_t bt_binary_weight_bytes(int64_t N, int64_t K)

@@ -287,6 +287,28 @@ bt_status bt_ternary_linear_rs(const void *Wp, const float *row_scale, const flo
                                void *stream);
 
 /*
+ * bt_ternary_linear_static -- bt_ternary_linear that allocates nothing and takes no
+ * workspace: for callers that cannot allocate device memory or pass one in (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation). Where
+ * bt_ternary_linear needs a workspace (bt_linear_workspace_bytes(M, N, K) > 0) this call
+ * uses a scratch array of BT_STATIC_SCRATCH_BYTES bytes that the library holds on every
+ * GPU it runs on until the process ends (its address is looked up once per device, on the
+ * first such call there). The caller still owns X, Y and acc.
+ *   Arguments, routes and results are those of bt_ternary_linear: bit-identical outputs.
+ *   Limit: bt_linear_workspace_bytes(M, N, K) <= BT_STATIC_SCRATCH_BYTES, else
+ *   BT_ERR_UNSUPPORTED and nothing is enqueued (2B-class prefill at 2048 tokens needs about
+ *   31 MB of it).
+ *   Concurrency: every call on one GPU shares that GPU's scratch. Calls whose kernels may
+ *   overlap (different streams, or other host threads) race and give undefined results;
+ *   serialize them (one stream, or events). A call writes all the scratch it reads before
+ *   reading it (the quantizer zero-fills the GEMM's arrival counters), so no clearing is
+ *   needed between calls.
+ */
+#define BT_STATIC_SCRATCH_BYTES 67108864LL
+bt_status bt_ternary_linear_static(const void *Wp, const float *w_scale, const float *X, int64_t M, int64_t N,
+                                   int64_t K, float *Y, int32_t *acc, void *stream);
+
+/*
  * 1-bit activations: the binary GEMV (W1A1) and ternary weights against binarized
  * tokens (W1.58A1). Follows the "bit-floor" page, "The core math" (binary GEMV =
  * 2 * POPCNT(XNOR(W, x)) - K over packed sign bits; ternary GEMV = POPCNT(mag &
