@@ -81,6 +81,15 @@ def parse():
                    help="row-group weight scales: fused Q/K/V and gate/up matrices packed with one scale per "
                         "block (bt_pack_weights_rows), products through the row-scale entry points")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the achievable-ceiling kernels (launch floor, plain reads, MFMA loop)")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="2b_decode only: skip the prefill half of the metric (2B prefill GEMM at M = 2048)")
+    p.add_argument("--cpu-cores", type=int, default=None,
+                   help="worker processes of the all-cores oracle baseline (default: the usable cores, at most 16)")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
+                   help="write a per-kernel summary (durations and launch intervals) of a rocprofv3 --kernel-trace "
+                        "--stats run of this workload")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain 1 GiB device copy 10 times (HBM counter calibration)")
@@ -294,6 +303,16 @@ def run_gpu(args, spec):
         stream.synchronize()
         ms_step = timed(step, args.steps, args.warmup)
         ms_prod = ms_step if fused else timed(products, args.steps, args.warmup)
+        # per matrix shape: the product launches of that shape alone (one per layer)
+        shape_us = []
+        for j in range(len(shapes)):
+            def one_shape(j=j):
+                for row in packed:
+                    if fused:
+                        bt.linear(xs[j], row[j], out_y=ys[j])
+                    else:
+                        product(row[j], qs[j], ys[j], j)
+            shape_us.append(timed(one_shape, args.steps, args.warmup) * 1e3 / spec["layers"])
 
     step_bytes = step_ops = prod_bytes = 0
     for row in packed:
@@ -309,7 +328,143 @@ def run_gpu(args, spec):
     n_prod = spec["layers"] * len(shapes)
     return dict(ms_step=ms_step, ms_prod=ms_prod, step_bytes=step_bytes, step_ops=step_ops,
                 prod_bytes=prod_bytes, n_prod=n_prod, resident=resident, setup_s=setup_s,
-                launch="eager" if args.eager else "hipGraph", fused=fused, kernel=kernel)
+                launch="eager" if args.eager else "hipGraph", fused=fused, kernel=kernel, shape_us=shape_us,
+                packed=packed, stream=stream, timed=timed)
+
+
+# ------------------------------------------------------- achievable ceilings
+def ceilings_lib():
+    """libbt_ceilings.so: the empty-launch, plain-read and MFMA-loop kernels (built with libbt.so)."""
+    import ctypes
+
+    path = os.path.join(ROOT, "bit_ternary_weight_absmean_amd", "libbt_ceilings.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run `python -m bit_ternary_weight_absmean_amd.build`")
+    L = ctypes.CDLL(path)
+    i32, i64, vp, u32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint32
+    L.btc_launch_empty.argtypes = [i32, i32, i32, vp, vp]
+    L.btc_read_blocks.argtypes = [i64, i32]
+    L.btc_launch_read.argtypes = [vp, i64, i32, vp, vp]
+    L.btc_launch_mfma.argtypes = [i32, i32, u32, vp, vp]
+    for f in (L.btc_launch_empty, L.btc_read_blocks, L.btc_launch_read, L.btc_launch_mfma):
+        f.restype = i32
+    return L
+
+
+LARGE_READ_BYTES = 117_440_512  # the 100B-class gate+up matrix packed at 2 bits
+MFMA_OPS = 2 * 16 * 16 * 64     # one v_mfma_i32_16x16x64_i8
+
+
+def run_ceilings(args, spec, g):
+    """What the hardware gives this workload with no method arithmetic: the launch floor of
+    the step's graph, a plain read of each resident matrix in the step's launch structure,
+    a plain read of a large matrix, and the int8 MFMA rate (bench.py --ceilings alone, or
+    detail.ceilings of the default run)."""
+    import torch
+
+    L = ceilings_lib()
+    stream, timed, packed = g["stream"], g["timed"], g["packed"]
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device=dev)
+    out, s = sink.data_ptr(), stream.cuda_stream
+    n_launch = g["n_prod"]
+    steps, warmup = max(args.steps, 5), max(args.warmup, 2)
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"ceiling kernel launch failed (hipError {rc})")
+
+    res = {}
+    with torch.cuda.stream(stream):
+        # launch floor: the graph of n_launch back-to-back launches, at the first matrix's grid
+        _, N0, _ = spec["shapes"][0]
+        grid0 = -(-N0 // 16)  # one workgroup per 16-row block at most: an upper bound on the fused grid
+        for store in (0, 1):
+            def empties(store=store):
+                for _ in range(n_launch):
+                    ok(L.btc_launch_empty(grid0, 512, store, out, s))
+            res["launch_floor_store_us" if store else "launch_floor_us"] = round(
+                timed(empties, steps, warmup) * 1e3 / n_launch, 3)
+        # plain read of each resident matrix, one launch per matrix as in the step, best of four
+        # loads-per-thread choices
+        per_shape, best_u = {}, {}
+        for j, (name, N, K) in enumerate(spec["shapes"]):
+            nbytes = packed[0][j].data.numel()
+            best = None
+            for u in (1, 2, 4, 8):
+                def reads(u=u, j=j, nbytes=nbytes):
+                    for row in packed:
+                        ok(L.btc_launch_read(row[j].data.data_ptr(), nbytes, u, out, s))
+                us = timed(reads, steps, warmup) * 1e3 / len(packed)
+                if best is None or us < best[0]:
+                    best = (us, u)
+            best_u[j] = best[1]
+            per_shape[name] = {"bytes": nbytes, "read_us": round(best[0], 3),
+                               "read_GBs": round(nbytes / (best[0] * 1e-6) / 1e9, 1),
+                               "product_us": round(g["shape_us"][j], 3),
+                               "product_frac_of_read": round(best[0] / g["shape_us"][j], 4)}
+
+        def read_step():
+            for row in packed:
+                for j, pw in enumerate(row):
+                    ok(L.btc_launch_read(pw.data.data_ptr(), pw.data.numel(), best_u[j], out, s))
+        read_ms = timed(read_step, steps, warmup)
+        res["per_shape"] = per_shape
+        res["read_step_ms"] = round(read_ms, 5)
+        read_bytes = sum(pw.data.numel() for row in packed for pw in row)
+        res["read_step_GBs"] = round(read_bytes / (read_ms * 1e-3) / 1e9, 1)
+        res["step_frac_of_read_step"] = round(read_ms / g["ms_step"], 4)
+        # a large plain read (three rotating buffers, 352 MB: more than the 256 MB Infinity Cache)
+        bufs = [torch.empty(LARGE_READ_BYTES, dtype=torch.uint8, device=dev) for _ in range(3)]
+        for b in bufs:
+            b.fill_(1)
+        best = None
+        for u in (2, 4, 8):
+            def big(u=u):
+                for _ in range(2):
+                    for b in bufs:
+                        ok(L.btc_launch_read(b.data_ptr(), LARGE_READ_BYTES, u, out, s))
+            us = timed(big, steps, warmup) * 1e3 / 6
+            best = us if best is None else min(best, us)
+        res["large_read"] = {"bytes": LARGE_READ_BYTES, "us": round(best, 2),
+                             "GBs": round(LARGE_READ_BYTES / (best * 1e-6) / 1e9, 1)}
+        del bufs
+        # int8 MFMA loop at one to three waves per SIMD
+        iters = 4000
+        mf = {}
+        for wps in (1, 2, 3, 4):
+            blocks = 256 * wps
+
+            def loop(blocks=blocks):
+                ok(L.btc_launch_mfma(blocks, iters, 12345, out, s))
+            ms = timed(loop, 5, 2)
+            mf[wps] = blocks * 4 * iters * 16 * MFMA_OPS / (ms * 1e-3) / 1e12
+        wps = max(mf, key=mf.get)
+        res["mfma_int8_TOPS"] = round(mf[wps], 1)
+        res["mfma_waves_per_simd"] = wps
+        res["mfma_int8_TOPS_by_waves_per_simd"] = {str(k): round(v, 1) for k, v in mf.items()}
+        # a library dense int8 GEMM (torch._int_mm: hipBLASLt / rocBLAS) of the 2B prefill gate+up
+        # shape on unpacked int8 operands, for reference
+        try:
+            A = torch.randint(-127, 128, (2048, 2560), dtype=torch.int8, device=dev)
+            B = torch.randint(-1, 2, (13824, 2560), dtype=torch.int8, device=dev).t()
+            torch._int_mm(A, B)
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(20):
+                torch._int_mm(A, B)
+            ev1.record(stream)
+            ev1.synchronize()
+            ms = ev0.elapsed_time(ev1) / 20
+            res["library_int8_gemm"] = {"shape": "2048 x 13824 x 2560 (torch._int_mm, int8 in, int32 out)",
+                                        "us": round(ms * 1e3, 2),
+                                        "TOPS": round(2 * 2048 * 13824 * 2560 / (ms * 1e-3) / 1e12, 1)}
+            del A, B
+        except Exception as e:  # reported, not fatal: the reference is optional
+            res["library_int8_gemm"] = {"error": str(e)[:200]}
+    torch.cuda.synchronize()
+    return res
 
 
 # ------------------------------------------------- 1-bit activations (W1A1, W1.58A1)
@@ -451,44 +606,131 @@ def run_onebit_cpu_baseline(args, M):
 
 
 # ----------------------------------------------------------- CPU baseline leg
+# Matrices of the CPU sample, inherited by the all-cores worker processes (fork).
+_CPU_MATS = []
+
+
+def _cpu_rows(task):
+    """Worker of the all-cores baseline: the oracle's int32 triple loop on a block of
+    output rows of one sample matrix."""
+    import oracle
+
+    i, r0, r1, Q = task
+    T = _CPU_MATS[i][0]
+    return i, r0, oracle.ternary_matmul(T[r0:r1], Q)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def usable_cores(limit=16):
+    """Cores this process may run on, at most `limit` (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, limit))
+
+
 def run_cpu_baseline(args, spec):
-    """The oracle as it stands, single-threaded, on a bounded sample of the same workload:
-    layer 0's matrices (all four shapes; for prefill the first 16 tokens), repeated until
-    about --cpu-seconds of CPU work."""
+    """The oracle as it stands, on a bounded sample of the same workload: layer 0's matrices
+    (all four shapes; for prefill the first 16 tokens), repeated until about --cpu-seconds
+    of work, first single-threaded, then with the int32 triple loop -- the dominant phase --
+    spread over the usable cores in row blocks (worker processes calling the same oracle
+    function; the results are identical, the sums being integer). Per-phase seconds are the
+    totals over the passes: quantize (per-token absmax int8), the int32 loop, the epilogue;
+    the offline weight scale + codes of each sample matrix are timed once."""
+    import multiprocessing as mp
+
+    import numpy as np
+
     import oracle
     from bit_ternary_weight_absmean_amd import synth
 
+    global _CPU_MATS
     M = spec["M"] if not spec["prefill"] else min(spec["M"], 16)
     cfg = spec["cfg"]
     lib = oracle.load()
     mats = []
+    t0 = time.perf_counter()
     for j, (_, N, K) in enumerate(spec["shapes"]):
         W = synth.layer_weight(cfg, 0, j, N, K)
         g = oracle.absmean(W, lib)
         mats.append((oracle.ternarize(W, g, lib), g, synth.layer_activation(cfg, j, M, K)))
         del W
-    done_bytes = done_ops = passes = 0
-    t0 = time.perf_counter()
-    while True:
-        for T, g, X in mats:
-            Q, s, qs = oracle.quant_act(X, lib)
-            acc = oracle.ternary_matmul(T, Q, lib)
-            oracle.scale_epilogue(acc, g, s, lib)
-            N, K = T.shape
-            done_bytes += linear_bytes(M, N, K)
-            done_ops += 2 * M * N * K
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds:
-            break
-    if spec["prefill"]:
-        value, unit = done_ops / el / 1e12, "TOPS"
-    else:
-        value, unit = done_bytes / el / 1e9, "GB/s"
-    return {"value": round(value, 4), "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": f"layer 0 of the workload ({len(mats)} matrices, M={M}), {passes} pass(es) in {el:.1f} s "
-                      "of the single-threaded C oracle (quantize + int32 triple loop + epilogue), bytes and ops "
-                      "counted as for the GPU step"}
+    pack_s = time.perf_counter() - t0
+    _CPU_MATS = mats
+    pass_bytes = sum(linear_bytes(M, T.shape[0], T.shape[1]) for T, _, _ in mats)
+    pass_ops = sum(2 * M * T.shape[0] * T.shape[1] for T, _, _ in mats)
+
+    def run(pool, cores):
+        ph = {"quantize": 0.0, "int32_loop": 0.0, "epilogue": 0.0}
+        passes = 0
+        accs = []
+        t_start = time.perf_counter()
+        while True:
+            accs = []
+            for i, (T, g, X) in enumerate(mats):
+                t = time.perf_counter()
+                Q, sx, _ = oracle.quant_act(X, lib)
+                ph["quantize"] += time.perf_counter() - t
+                t = time.perf_counter()
+                if pool is None:
+                    acc = oracle.ternary_matmul(T, Q, lib)
+                else:
+                    N = T.shape[0]
+                    step = -(-N // cores)
+                    acc = np.empty((M, N), np.int32)
+                    for _, r0, part in pool.imap_unordered(_cpu_rows, [(i, r0, min(N, r0 + step), Q)
+                                                                       for r0 in range(0, N, step)]):
+                        acc[:, r0:r0 + part.shape[1]] = part
+                ph["int32_loop"] += time.perf_counter() - t
+                t = time.perf_counter()
+                oracle.scale_epilogue(acc, g, sx, lib)
+                ph["epilogue"] += time.perf_counter() - t
+                accs.append(acc)
+            passes += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds / 2:
+                break
+        return passes, el, ph, accs
+
+    p1, el1, ph1, acc1 = run(None, 1)
+    cores = args.cpu_cores or usable_cores()
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        pool.map(_cpu_rows, [(0, 0, 1, oracle.quant_act(mats[0][2], lib)[0])] * cores)  # start the workers
+        pn, eln, phn, accn = run(pool, cores)
+    _CPU_MATS = []
+    for a, b in zip(acc1, accn):
+        if not np.array_equal(a, b):
+            raise RuntimeError("all-cores oracle baseline disagrees with the single-threaded one")
+
+    def rate(passes, el):
+        if spec["prefill"]:
+            return passes * pass_ops / el / 1e12
+        return passes * pass_bytes / el / 1e9
+
+    unit = "TOPS" if spec["prefill"] else "GB/s"
+    return {"value": round(rate(pn, eln), 4), "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"layer 0 of the workload ({len(mats)} matrices, M={M}) in passes of the C oracle "
+                      f"(quantize + int32 triple loop + epilogue; bytes and ops counted as for the GPU step): "
+                      f"{pn} passes in {eln:.1f} s with the int32 loop in row blocks over {cores} worker "
+                      f"processes; single-threaded {p1} passes in {el1:.1f} s",
+            "cpu_model": cpu_model(), "usable_cores": usable_cores(1 << 30),
+            "single_thread": {"value": round(rate(p1, el1), 4), "unit": unit, "passes": p1,
+                              "phases_s": {k: round(v, 3) for k, v in ph1.items()}},
+            "all_cores": {"value": round(rate(pn, eln), 4), "unit": unit, "passes": pn, "cores": cores,
+                          "phases_s": {k: round(v, 3) for k, v in phn.items()}},
+            "offline_scale_and_codes_s": round(pack_s, 3)}
 
 
 # ----------------------------------------------------------- counters
@@ -613,6 +855,74 @@ def summarize_mfma(args):
     print(json.dumps(out))
 
 
+def summarize_trace(args):
+    """Per-kernel summary of a rocprofv3 --kernel-trace --stats run of this workload: for every
+    kernel of this library, launches, mean and median duration (end - start of each dispatch)
+    and the mean interval from one dispatch's start to the next one's when they follow each
+    other inside a replayed graph (next start within 50 us). The interval is the per-launch
+    time the benchmark's HIP events measure (graph time over launches): short dispatches of a
+    graph overlap their completion with the next one's start, so their durations can sum to
+    more than the graph's time."""
+    import statistics
+
+    trace_dir, out_md = args.summarize_trace
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = collections.OrderedDict()
+    for i, r in enumerate(rows):
+        name = r["Kernel_Name"]
+        if not any(k in name for k in ("k_linear_decode", "k_gemv", "k_gemm", "k_quant_act", "k_read", "k_empty",
+                                       "k_store_one", "k_mfma_loop", "k_pack", "k_gamma", "k_row_abs_sum")):
+            continue
+        start, end = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        key = (name, r.get("Grid_Size", r.get("Grid_Size_X", "")), r.get("Workgroup_Size", ""))
+        e = per.setdefault(key, {"dur": [], "gap": []})
+        e["dur"].append((end - start) / 1e3)
+        if i + 1 < len(rows):
+            nxt = int(rows[i + 1]["Start_Timestamp"])
+            if 0 <= nxt - start <= 50_000:
+                e["gap"].append((nxt - start) / 1e3)
+    lines = [f"# Kernel trace: {args.workload} workload" + (f" (M={args.m})" if args.m else ""), "",
+             "Command (run from the repository root):", "", f"    {args.command}", "",
+             "Per kernel instance and launch shape: dispatch durations (end - start) and the interval from a",
+             "dispatch's start to the next dispatch's start inside a replayed graph (next start within 50 us;",
+             "the per-launch time that the benchmark's HIP events measure as graph time over launches).", "",
+             "| kernel | grid | WG | launches | mean us | median us | intervals | mean interval us | "
+             "median interval us |", "|---|---|---|---|---|---|---|---|---|"]
+    for (name, grid, wg), e in per.items():
+        d, gp = e["dur"], e["gap"]
+        lines.append(f"| `{name}` | {grid} | {wg} | {len(d)} | {statistics.mean(d):.3f} | {statistics.median(d):.3f} "
+                     f"| {len(gp)} | {statistics.mean(gp) if gp else float('nan'):.3f} | "
+                     f"{statistics.median(gp) if gp else float('nan'):.3f} |")
+    # every product kernel of the workload together
+    for kname in ("k_linear_decode", "k_gemv_staged", "k_gemv_direct", "k_gemm"):
+        d = [x for (n, _, _), e in per.items() if kname in n for x in e["dur"]]
+        gp = [x for (n, _, _), e in per.items() if kname in n for x in e["gap"]]
+        if d:
+            lines += ["", f"All `{kname}` dispatches: {len(d)}, mean duration {statistics.mean(d):.3f} us, "
+                          f"mean interval {statistics.mean(gp) if gp else float('nan'):.3f} us over {len(gp)} "
+                          "back-to-back pairs."]
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        lines += ["", "rocprofv3 `--stats` (kernel_stats.csv), this library's kernels:", "",
+                  "| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
+        with open(stats[0]) as fh:
+            for r in csv.DictReader(fh):
+                if any(k in r["Name"] for k in ("k_linear_decode", "k_gemv", "k_gemm", "k_quant_act", "k_read",
+                                                "k_empty", "k_store_one", "k_mfma_loop")):
+                    lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                                 f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def mfma_util_for(spec, kernel):
     """Mean MfmaUtil (%) from the committed counter summary, while the kernel sources still match."""
     if ROW_SCALES:
@@ -641,6 +951,21 @@ def traffic_for(spec, kernel):
 
 
 # ----------------------------------------------------------------- entry
+def prefill_detail(args, g, spec):
+    """The metric's second half: the 2B prefill GEMM step at M = 2048 (quantizer + GEMM per
+    matrix) and the GEMM launches alone against the int8 MFMA roofline."""
+    gemm_us = g["ms_prod"] * 1e3 / g["n_prod"]
+    ops_per_launch = g["step_ops"] / g["n_prod"]
+    ach = ops_per_launch / (gemm_us * 1e-6) / 1e12
+    return {"workload": spec["desc"], "M": spec["M"], "shapes": [f"{n} {N}x{K}" for n, N, K in spec["shapes"]],
+            "ms_per_step": round(g["ms_step"], 5), "step_TOPS": round(g["step_ops"] / (g["ms_step"] * 1e-3) / 1e12, 1),
+            "kernel": g["kernel"], "kernel_us_per_launch": round(gemm_us, 3),
+            "kernel_us_per_shape": {n: round(u, 3) for (n, _, _), u in zip(spec["shapes"], g["shape_us"])},
+            "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                         "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": traffic_for(spec, "k_gemm")},
+            "mfma_util_percent_counters": mfma_util_for(spec, "k_gemm")}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -653,6 +978,9 @@ def main():
         return 0
     if args.summarize_mfma:
         summarize_mfma(args)
+        return 0
+    if args.summarize_trace:
+        summarize_trace(args)
         return 0
     if args.calib_copy:
         calib_copy()
@@ -674,7 +1002,7 @@ def main():
         value = g["step_ops"] / (g["ms_step"] * 1e-3) / 1e12
         unit = "TOPS"
         ach = ops_per_launch / (prod_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                 "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": traffic}
     else:
         value = g["step_bytes"] / (g["ms_step"] * 1e-3) / 1e9
@@ -682,7 +1010,48 @@ def main():
         ach = bytes_per_launch / (prod_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+    ceil = None
+    if not args.no_ceilings:
+        ceil = run_ceilings(args, spec, g)
+    prefill = None
+    if args.workload == "2b_decode" and not args.no_prefill and not args.split:
+        # the metric's prefill half, in the same run: 2B prefill at 2048 tokens
+        pspec = workload_spec("2b_prefill", 2048)
+        if ROW_SCALES:
+            pspec["desc"] += ", row-group weight scales (one per Q, K, V and gate, up block)"
+        g.pop("packed")
+        gp = run_gpu(args, pspec)
+        prefill = prefill_detail(args, gp, pspec)
+        if ceil is not None:
+            prefill["roofline"]["achievable"] = ceil["mfma_int8_TOPS"]
+            prefill["roofline"]["frac_of_achievable"] = round(prefill["roofline"]["achieved"] /
+                                                              ceil["mfma_int8_TOPS"], 4)
+        del gp
+    elif spec["prefill"] and ceil is not None:
+        roof["achievable"] = ceil["mfma_int8_TOPS"]
+        roof["frac_of_achievable"] = round(ach / ceil["mfma_int8_TOPS"], 4)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, spec)
+    detail = {"dominant_kernel": g["kernel"],
+              "launch_interval_us": round(prod_us, 3),
+              "launch_interval_note": "product launches of one step replayed as a HIP graph, timed with HIP "
+                                      "events on their stream, divided by the launches: the per-launch time "
+                                      "roofline.achieved uses",
+              "kernel_us_per_shape": {n: round(u, 3) for (n, _, _), u in zip(spec["shapes"], g["shape_us"])},
+              "algorithmic_bytes_per_launch": round(bytes_per_launch),
+              "ops_per_launch": round(ops_per_launch),
+              "step_hbm_frac": None if spec["prefill"] else round(value / HBM_PEAK_GBS, 4),
+              "step_TOPS": round(g["step_ops"] / (g["ms_step"] * 1e-3) / 1e12, 3),
+              "weights_per_s": round(sum(N * K for _, N, K in spec["shapes"]) * spec["layers"] /
+                                     (g["ms_step"] * 1e-3), 1),
+              "setup_s": round(g["setup_s"], 1),
+              "mfma_util_percent_counters": mfma_util_for(spec, g["kernel"]) if spec["prefill"] else None}
+    if ceil is not None:
+        detail["launch_floor_us"] = ceil["launch_floor_us"]
+        detail["ceilings"] = ceil
+        if not spec["prefill"]:
+            detail["step_frac_of_read_ceiling"] = ceil["step_frac_of_read_step"]
+    if prefill is not None:
+        detail["prefill"] = prefill
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -705,15 +1074,7 @@ def main():
                             ("bt_ternary_gemm_ws" if g["kernel"] == "k_gemm" else "bt_ternary_gemv"))},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "detail": {"dominant_kernel": g["kernel"], "kernel_avg_us": round(prod_us, 3),
-                   "algorithmic_bytes_per_launch": round(bytes_per_launch),
-                   "ops_per_launch": round(ops_per_launch),
-                   "step_hbm_frac": None if spec["prefill"] else round(value / HBM_PEAK_GBS, 4),
-                   "step_TOPS": round(g["step_ops"] / (g["ms_step"] * 1e-3) / 1e12, 3),
-                   "weights_per_s": round(sum(N * K for _, N, K in spec["shapes"]) * spec["layers"] /
-                                          (g["ms_step"] * 1e-3), 1),
-                   "setup_s": round(g["setup_s"], 1),
-                   "mfma_util_percent_counters": mfma_util_for(spec, g["kernel"]) if spec["prefill"] else None},
+        "detail": detail,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -3,7 +3,8 @@
     python -m bit_ternary_weight_absmean_amd.build
 
 Each .hip source is compiled to an object in parallel, then linked into
-``bit_ternary_weight_absmean_amd/libbt.so``.
+``bit_ternary_weight_absmean_amd/libbt.so``; the benchmark's ceiling kernels go into
+``libbt_ceilings.so`` beside it.
 """
 from __future__ import annotations
 
@@ -19,6 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libbt.so")
+# The benchmark's ceiling kernels (empty launch, plain read, MFMA loop): a library of their
+# own, not part of libbt.so.
+CEILINGS_SRC = "ceilings.hip"
+CEILINGS_LIB = os.path.join(PKG, "libbt_ceilings.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "lut.hip", "bits.hip", "decode.hip", "gemm.hip"]
@@ -51,9 +56,14 @@ def hipcc() -> str:
     return path
 
 
+# Per-source extra flags. The MFMA-loop ceiling keeps its sixteen accumulators in VGPRs:
+# with AGPR accumulators the compiler copies them between AGPRs inside the loop.
+EXTRA_FLAGS = {CEILINGS_SRC: ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
@@ -71,8 +81,15 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    obj = _compile(CEILINGS_SRC)
+    tmp = CEILINGS_LIB + ".tmp"
+    res = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj], capture_output=True,
+                         text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, CEILINGS_LIB)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {CEILINGS_LIB}")
     return LIB_PATH
 
 
