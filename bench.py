@@ -303,16 +303,22 @@ def run_gpu(args, spec):
         stream.synchronize()
         ms_step = timed(step, args.steps, args.warmup)
         ms_prod = ms_step if fused else timed(products, args.steps, args.warmup)
-        # per matrix shape: the product launches of that shape alone (one per layer)
+        # per matrix shape, in the context of the step: the product graph's time minus that of
+        # the same graph without the shape's launches, over the layers (a graph of one shape
+        # alone would re-read a few matrices from the Infinity Cache and carry the replay's
+        # fixed cost on few launches)
         shape_us = []
         for j in range(len(shapes)):
-            def one_shape(j=j):
+            def all_but(j=j):
                 for row in packed:
-                    if fused:
-                        bt.linear(xs[j], row[j], out_y=ys[j])
-                    else:
-                        product(row[j], qs[j], ys[j], j)
-            shape_us.append(timed(one_shape, args.steps, args.warmup) * 1e3 / spec["layers"])
+                    for jj, pw in enumerate(row):
+                        if jj == j:
+                            continue
+                        if fused:
+                            bt.linear(xs[jj], pw, out_y=ys[jj])
+                        else:
+                            product(pw, qs[jj], ys[jj], jj)
+            shape_us.append((ms_prod - timed(all_but, args.steps, args.warmup)) * 1e3 / spec["layers"])
 
     step_bytes = step_ops = prod_bytes = 0
     for row in packed:
@@ -385,30 +391,33 @@ def run_ceilings(args, spec, g):
                     ok(L.btc_launch_empty(grid0, 512, store, out, s))
             res["launch_floor_store_us" if store else "launch_floor_us"] = round(
                 timed(empties, steps, warmup) * 1e3 / n_launch, 3)
-        # plain read of each resident matrix, one launch per matrix as in the step, best of four
-        # loads-per-thread choices
-        per_shape, best_u = {}, {}
-        for j, (name, N, K) in enumerate(spec["shapes"]):
-            nbytes = packed[0][j].data.numel()
-            best = None
-            for u in (1, 2, 4, 8):
-                def reads(u=u, j=j, nbytes=nbytes):
-                    for row in packed:
-                        ok(L.btc_launch_read(row[j].data.data_ptr(), nbytes, u, out, s))
-                us = timed(reads, steps, warmup) * 1e3 / len(packed)
-                if best is None or us < best[0]:
-                    best = (us, u)
-            best_u[j] = best[1]
-            per_shape[name] = {"bytes": nbytes, "read_us": round(best[0], 3),
-                               "read_GBs": round(nbytes / (best[0] * 1e-6) / 1e9, 1),
-                               "product_us": round(g["shape_us"][j], 3),
-                               "product_frac_of_read": round(best[0] / g["shape_us"][j], 4)}
-
-        def read_step():
+        # plain read of each resident matrix, one launch per matrix as in the step: the loads per
+        # thread (1, 2, 4 or 8) that give the fastest read step, then each shape's time in that
+        # step's context (the step's time minus that of the step without the shape's reads)
+        def read_step(us_of=None, skip=None):
             for row in packed:
                 for j, pw in enumerate(row):
-                    ok(L.btc_launch_read(pw.data.data_ptr(), pw.data.numel(), best_u[j], out, s))
-        read_ms = timed(read_step, steps, warmup)
+                    if j != skip:
+                        ok(L.btc_launch_read(pw.data.data_ptr(), pw.data.numel(), us_of[j], out, s))
+        nshape = len(spec["shapes"])
+        best_u = [1] * nshape
+        for j in range(nshape):
+            best = None
+            for u in (1, 2, 4, 8):
+                trial = list(best_u)
+                trial[j] = u
+                ms = timed(lambda: read_step(trial), steps, warmup)
+                if best is None or ms < best[0]:
+                    best = (ms, u)
+            best_u[j] = best[1]
+        read_ms = timed(lambda: read_step(best_u), steps, warmup)
+        per_shape = {}
+        for j, (name, N, K) in enumerate(spec["shapes"]):
+            nbytes = packed[0][j].data.numel()
+            us = (read_ms - timed(lambda: read_step(best_u, j), steps, warmup)) * 1e3 / len(packed)
+            per_shape[name] = {"bytes": nbytes, "read_us": round(us, 3), "read_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                               "loads_per_thread": best_u[j], "product_us": round(g["shape_us"][j], 3),
+                               "product_frac_of_read": round(us / g["shape_us"][j], 4)}
         res["per_shape"] = per_shape
         res["read_step_ms"] = round(read_ms, 5)
         read_bytes = sum(pw.data.numel() for row in packed for pw in row)
