@@ -235,23 +235,29 @@ def run_gpu(args, spec):
         gws.append(bt.gemm_workspace(M, N, K, dev) if M > bt.GEMV_MAX_M else None)
     torch.cuda.synchronize()
 
-    fused = (not args.split) and all(bt.linear_workspace_bytes(M, N, K) == 0 for _, N, K in shapes)
-    if fused:
-        kernel = "k_linear_decode"
-    elif spec["prefill"] or M > bt.GEMV_MAX_M:
-        kernel = "k_gemm"
-    else:
-        names = {"mfma": "k_gemv_direct", "staged": "k_gemv_staged", "dot4": "k_gemv_dot4", "lut": "k_gemv_lut"}
-        if args.gemv_algo == "auto":  # the library's pick per shape (BT_GEMV_AUTO), as bt_ternary_linear makes it
-            picks = ["staged" if M * ((K + 255) // 256 * 256) <= 131072 else "mfma" for _, _, K in shapes]
-            kernel = " + ".join(dict.fromkeys(names[c] for c in picks))
-        else:
-            kernel = names[args.gemv_algo]
+    # Route of each matrix shape, as the step runs it: the fused decode kernel where
+    # bt_ternary_linear takes it (no workspace), else the product kernel on activations the
+    # quantizer launch wrote (--split: always the latter).
+    fused_j = [(not args.split) and bt.linear_workspace_bytes(M, N, K) == 0 for _, N, K in shapes]
+    fused = all(fused_j)
+    gemm = spec["prefill"] or M > bt.GEMV_MAX_M
+    names = {"mfma": "k_gemv_direct", "staged": "k_gemv_staged", "dot4": "k_gemv_dot4", "lut": "k_gemv_lut"}
+
+    def kernel_of(j):
+        _, N, K = shapes[j]
+        if fused_j[j]:
+            return "k_linear_decode"
+        if gemm:
+            return "k_gemm"
+        if args.gemv_algo == "auto":  # the library's pick (BT_GEMV_AUTO), as bt_ternary_linear makes it
+            return names["staged" if M * ((K + 255) // 256 * 256) <= 131072 else "mfma"]
+        return names[args.gemv_algo]
+    kernel = " + ".join(dict.fromkeys(kernel_of(j) for j in range(len(shapes))))
     algo = {"auto": bt.GEMV_AUTO, "mfma": bt.GEMV_MFMA, "staged": bt.GEMV_STAGED, "dot4": bt.GEMV_DOT4,
             "lut": bt.GEMV_LUT}[args.gemv_algo]
 
     def product(pw, q, out_y, j):
-        if kernel == "k_gemm":
+        if gemm:
             return bt.ternary_gemm(pw, q, out_y=out_y, workspace=gws[j])
         return bt.ternary_gemv(pw, q, out_y=out_y, algo=algo)
 
@@ -265,10 +271,11 @@ def run_gpu(args, spec):
                     bt.linear(xs[j], pw, out_y=ys[j], workspace=wss[j])
 
     def products():
-        """Only the dominant kernel's launches of one step (activations already quantized)."""
+        """The product launches of one step: the fused kernel where the step runs it, else the
+        product kernel on the already quantized activations (the quantizer launches left out)."""
         for row in packed:
             for j, pw in enumerate(row):
-                if fused:
+                if fused_j[j]:
                     bt.linear(xs[j], pw, out_y=ys[j])
                 else:
                     product(pw, qs[j], ys[j], j)
@@ -314,7 +321,7 @@ def run_gpu(args, spec):
                     for jj, pw in enumerate(row):
                         if jj == j:
                             continue
-                        if fused:
+                        if fused_j[jj]:
                             bt.linear(xs[jj], pw, out_y=ys[jj])
                         else:
                             product(pw, qs[jj], ys[jj], jj)
@@ -324,7 +331,7 @@ def run_gpu(args, spec):
     for row in packed:
         for j, (_, N, K) in enumerate(shapes):
             # the fused kernel reads fp32 x once and never writes or re-reads int8 Xq
-            if fused:
+            if fused_j[j]:
                 step_bytes += linear_bytes(M, N, K)
                 prod_bytes += linear_bytes(M, N, K)
             else:
@@ -334,7 +341,8 @@ def run_gpu(args, spec):
     n_prod = spec["layers"] * len(shapes)
     return dict(ms_step=ms_step, ms_prod=ms_prod, step_bytes=step_bytes, step_ops=step_ops,
                 prod_bytes=prod_bytes, n_prod=n_prod, resident=resident, setup_s=setup_s,
-                launch="eager" if args.eager else "hipGraph", fused=fused, kernel=kernel, shape_us=shape_us,
+                launch="eager" if args.eager else "hipGraph", fused=fused, fused_any=any(fused_j), kernel=kernel,
+                shape_us=shape_us,
                 packed=packed, stream=stream, timed=timed)
 
 
@@ -1147,6 +1155,8 @@ def main():
                    "shapes": [f"{n} {N}x{K}" for n, N, K in spec["shapes"]],
                    "resident_packed_bytes": g["resident"], "launch": g["launch"],
                    "step": ("per matrix: bt_ternary_linear (quantizer fused into the decode kernel)" if g["fused"]
+                            else "per matrix: bt_ternary_linear (the fused decode kernel where it takes the "
+                                 "shape, else bt_quant_act + bt_ternary_gemv)" if g["fused_any"]
                             else ("per matrix: bt_quant_act + " if args.split else
                                   "per matrix: bt_ternary_linear = bt_quant_act + ") +
                             ("bt_ternary_gemm_ws" if g["kernel"] == "k_gemm" else "bt_ternary_gemv"))},
