@@ -558,7 +558,17 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
                 s_qpart[m * WAVES + wave] = sum;
         }
     }
-    __syncthreads();
+    if constexpr (regpath && S == WAVES) {
+        // One row block per workgroup: thread tid quantized float4 tid + i * T, the 256-k
+        // step wave + 8 i, which is exactly the step the wave's MFMAs take as k-split
+        // wave; and its sums of q fold into its own partials. Each wave therefore reads
+        // back only LDS it wrote itself: its own writes retiring is all it waits for.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+        __syncthreads();
+    }
 
     // 5. Stream the wave's weights, two batches in flight, MFMAs on the older one.
     //    Token columns r >= M read token M - 1 (their outputs are never stored); every
