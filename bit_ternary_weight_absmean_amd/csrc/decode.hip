@@ -359,7 +359,9 @@ __host__ __device__ constexpr int fused_pitch(int KC4, int rx)
 // Every instruction between the arrival of the activations and the stores is on the
 // launch's critical path (at 2B sizes the weights are in registers well before the
 // quantizer is done), and a SIMD runs two of the eight waves: the work that does not
-// need the token maxima is done before or after the two barriers around the quantizer.
+// need the token maxima is done before or after the barriers around the quantizer (one,
+// after the absmax, with one row block per workgroup: each wave then reads back only the
+// activations it quantized itself; two otherwise).
 template <int MT, int S, int RX, int U, bool ROWS>
 __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const float *__restrict__ X,
@@ -380,9 +382,10 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
     constexpr bool regpath = RX > 0;  // then K4 >= 1 and K4 <= RX * T (the launcher checks)
     // One row block per workgroup (S = 8): all eight waves' partials meet in the k-split
     // sum, so each wave subtracts its own share of sum_k q there instead of publishing it
-    // before the second barrier.
+    // to the other waves.
     constexpr bool fold_q = regpath && RBW == 1;
-    // Register path with k-splits: the wave sums of q are formed after the second barrier.
+    // Register path with k-splits: the wave sums of q are formed after the quantizer's
+    // LDS stores, off the path to the first MFMA.
     constexpr bool late_q = regpath && S > 1;
     constexpr int KE = S - 1;         // the k-split that runs the epilogue
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
