@@ -14,8 +14,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped (not silently passed) when no GPU is visible; on a GPU
-    # box they run and fail loudly if the HIP library is missing.
+    # GPU tests are skipped (not silently passed) when no GPU is visible; on a machine
+    # with a GPU they run and fail loudly if the HIP library is missing.
     try:
         import torch
 
