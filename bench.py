@@ -59,6 +59,7 @@ KERNEL_SOURCES = {
     "k_linear_decode": ["decode.hip", "wave.h", "bt_internal.h"],
     "k_gemv_direct": ["decode.hip", "wave.h", "bt_internal.h"],
     "k_gemv_staged": ["decode.hip", "wave.h", "bt_internal.h"],
+    "k_gemv_blocked": ["decode.hip", "wave.h", "bt_internal.h"],
     "k_gemv_dot4": ["gemv.hip", "bt_internal.h"],
     "k_gemv_lut": ["lut.hip", "bt_internal.h"],
     "k_gemm": ["gemm.hip", "bt_internal.h"],
@@ -243,14 +244,17 @@ def run_gpu(args, spec):
     gemm = spec["prefill"] or M > bt.GEMV_MAX_M
     names = {"mfma": "k_gemv_direct", "staged": "k_gemv_staged", "dot4": "k_gemv_dot4", "lut": "k_gemv_lut"}
 
+    def staged_name(N, K):  # whole rows in LDS, or rows staged in K-blocks
+        return "k_gemv_staged" if M * ((K + 255) // 256 * 256) <= 131072 else "k_gemv_blocked"
+
     def kernel_of(j):
         _, N, K = shapes[j]
         if fused_j[j]:
             return "k_linear_decode"
         if gemm:
             return "k_gemm"
-        if args.gemv_algo == "auto":  # the library's pick (BT_GEMV_AUTO), as bt_ternary_linear makes it
-            return names["staged" if M * ((K + 255) // 256 * 256) <= 131072 else "mfma"]
+        if args.gemv_algo in ("auto", "staged"):  # BT_GEMV_AUTO takes the staged forms, as bt_ternary_linear
+            return staged_name(N, K)
         return names[args.gemv_algo]
     kernel = " + ".join(dict.fromkeys(kernel_of(j) for j in range(len(shapes))))
     algo = {"auto": bt.GEMV_AUTO, "mfma": bt.GEMV_MFMA, "staged": bt.GEMV_STAGED, "dot4": bt.GEMV_DOT4,
@@ -916,7 +920,7 @@ def summarize_trace(args):
                      f"| {len(gp)} | {statistics.mean(gp) if gp else float('nan'):.3f} | "
                      f"{statistics.median(gp) if gp else float('nan'):.3f} |")
     # every product kernel of the workload together
-    for kname in ("k_linear_decode", "k_gemv_staged", "k_gemv_direct", "k_gemm"):
+    for kname in ("k_linear_decode", "k_gemv_staged", "k_gemv_blocked", "k_gemv_direct", "k_gemm"):
         d = [x for (n, _, _), e in per.items() if kname in n for x in e["dur"]]
         gp = [x for (n, _, _), e in per.items() if kname in n for x in e["gap"]]
         if d:

@@ -224,14 +224,11 @@ static bt_status gemv_impl(const void *Wp, const float *w_scale, bool rows, cons
     if (algo == BT_GEMV_AUTO)
         // Measured on the 2B, 7B and 100B decode shapes at 1 to 16 tokens: staging the
         // int8 rows in LDS once per workgroup beats re-reading them per step (k_gemv_direct)
-        // by 20-30% at every size that fits.
-        algo = bt::gemv_staged_fits(M, N, K) ? BT_GEMV_STAGED : BT_GEMV_MFMA;
-    if (algo == BT_GEMV_STAGED) {
-        if (K == 0)
-            algo = BT_GEMV_MFMA;
-        else if (!bt::gemv_staged_fits(M, N, K))
-            return fail(BT_ERR_UNSUPPORTED, "staged gemv takes M <= 16 with M * K (rounded up to 256) <= 131072");
-    }
+        // by 20-30% at every size that fits whole, and rows too long for that are staged in
+        // K-blocks (k_gemv_blocked).
+        algo = BT_GEMV_STAGED;
+    if (algo == BT_GEMV_STAGED && K == 0)
+        algo = BT_GEMV_MFMA;
     if (algo == BT_GEMV_DOT4 && M > 4)
         return fail(BT_ERR_UNSUPPORTED, "dot4 gemv takes M <= 4 (got %lld)", (long long)M);
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -584,15 +581,13 @@ bt_status bt_kernel_plan(int32_t call, int64_t M, int64_t N, int64_t K, int32_t 
         if (M > BT_GEMV_MAX_M)
             return fail(BT_ERR_UNSUPPORTED, "gemv takes M <= %d", BT_GEMV_MAX_M);
         if (a == BT_GEMV_AUTO)
-            a = bt::gemv_staged_fits(M, N, K) ? BT_GEMV_STAGED : BT_GEMV_MFMA;
+            a = BT_GEMV_STAGED;
         if (a == BT_GEMV_STAGED && K == 0)
             a = BT_GEMV_MFMA;
         if (a == BT_GEMV_LUT && K == 0)
             a = BT_GEMV_MFMA;
         switch (a) {
         case BT_GEMV_STAGED:
-            if (!bt::gemv_staged_fits(M, N, K))
-                return fail(BT_ERR_UNSUPPORTED, "staged gemv does not take this shape");
             add(bt::plan_gemv_staged(M, N, K, rows, buf + used, room()));
             return ok();
         case BT_GEMV_MFMA: add(bt::plan_gemv_mfma(M, N, K, rows, buf + used, room())); return ok();

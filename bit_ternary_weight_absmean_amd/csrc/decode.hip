@@ -858,6 +858,203 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv_staged(
     }
 }
 
+// ------------------------------------------------------------ blocked kernel
+// k_gemv_staged for int8 rows too long to stage whole (M * K above the staged kernel's LDS
+// limit, e.g. 16 tokens x 28672): K is walked in blocks of KB = BPB * S * U steps of 256 k,
+// so that every wave owns exactly BPB (1 or 2) weight batches of each block and all waves run
+// the same number of blocks (and barriers). Block kb's rows sit in LDS buffer kb % 2, in the staged
+// kernel's transposed chunk layout; block kb + 1's chunks are loaded into registers when
+// block kb starts (global -> registers, two 64-byte chunks per thread), written into the
+// other buffer once block kb's MFMAs are issued, and published by the one barrier per block.
+// The weight stream keeps two batches in flight across the block boundaries.
+template <int S, int U, int BPB, bool ROWS>
+__global__ __launch_bounds__(kFusedWaves * 64) void k_gemv_blocked(
+    const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq,
+    float *__restrict__ Y, int32_t *__restrict__ ACC, int M, int N, int K, const float *__restrict__ sx_in,
+    const int32_t *__restrict__ xsum_in)
+{
+    constexpr int WAVES = kFusedWaves;
+    constexpr int T = WAVES * 64;
+    constexpr int RBW = WAVES / S;
+    constexpr int KE = S - 1;
+    constexpr int KB = BPB * S * U;      // steps per block
+    constexpr int KBC = 4 * KB;          // 64-byte chunks per token and block
+    constexpr int CH = 2;                // chunks each thread copies per block (M * KBC <= 2 * T)
+    constexpr int BPITCH = KBC * 64 + kPitchPad;
+    const int KC = (K + 63) >> 6;
+    const int NB16 = ((N + 63) >> 6) * 4;
+    const int KC4 = (KC + 3) & ~3;
+    const int ldq = KC4 * 64;
+    const int nsteps = KC4 >> 2;
+    const int nblocks = (nsteps + KB - 1) / KB;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    int4 *red = reinterpret_cast<int4 *>(smem);  // [WAVES][64] (S > 1)
+    int8_t *xbuf = reinterpret_cast<int8_t *>(smem + (S > 1 ? WAVES * 64 * 16 : 0));  // 2 x [M][BPITCH]
+    const int bufbytes = M * BPITCH;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int g = lane >> 4;
+    const int r = lane & 15;
+    const int ks = wave % S;
+    const int b16 = blockIdx.x * RBW + wave / S;
+    const int nchunks = M * KBC;
+
+    // Chunk i of this thread in block kb: token m, row chunk c (clamped into the row; slots
+    // past the last step are never read).
+    v4i cb[CH][4];
+    auto load_block = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int ch = min(tid + i * T, nchunks - 1);
+            const int m = ch / KBC, cl = ch - m * KBC;
+            const int c = min(kb * KBC + cl, KC4 - 1);
+            const v4i *src = reinterpret_cast<const v4i *>(Xq + (int64_t)m * ldq + c * 64);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                cb[i][q] = src[q];
+        }
+    };
+    auto store_block = [&](int kb) {
+        int8_t *dstbuf = xbuf + (kb & 1) * bufbytes;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int ch = tid + i * T;
+            if (ch < nchunks) {
+                const int m = ch / KBC, cl = ch - m * KBC;
+                v4i *dst = reinterpret_cast<v4i *>(dstbuf + m * BPITCH + cl * 64);
+#pragma unroll
+                for (int sidx = 0; sidx < 4; ++sidx)
+                    dst[sidx] = v4i{cb[i][0][sidx], cb[i][1][sidx], cb[i][2][sidx], cb[i][3][sidx]};
+            }
+        }
+    };
+
+    // 1. Block 0's chunks, then the wave's first two weight batches (block 0's), then the
+    //    epilogue's inputs.
+    load_block(0);
+    __builtin_amdgcn_sched_barrier(0);
+    const int nmine = (ks < nsteps) ? (nsteps - 1 - ks) / S + 1 : 0;
+    const int nb = (nmine + U - 1) / U;
+    v4i wa[U], wb[U];
+    auto load_batch = [&](v4i (&w)[U], int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            w[u] = load_w_raw(Wp, b16, NB16, 4 * (ks + S * (b * U + u)) + g, KC, r);
+    };
+    load_batch(wa, 0);  // K >= 1: valid clamped addresses
+    load_batch(wb, 1);
+    float4 gam;
+    if constexpr (ROWS) {
+        gam = load_scales4(w_scale, (int64_t)b16 * 16 + 4 * g, N, true);
+    } else {
+        const float g1 = load_scale_vmem(w_scale);
+        gam = make_float4(g1, g1, g1, g1);
+    }
+    const int rt = min(r, M - 1);
+    const float sx_r = sx_in[rt];
+    const int qs_r = xsum_in[rt];
+    store_block(0);
+    __syncthreads();
+
+    // 2. Block by block: the next block's chunks go out first, then block kb's BPB batches
+    //    (MFMAs on LDS buffer kb % 2, the batch two ahead loaded behind each), then the next
+    //    block into the other buffer and the block's barrier.
+    v4i a1 = v4i{0, 0, 0, 0}, a4 = a1, a16 = a1;
+    auto compute_batch = [&](const v4i (&w)[U], int b, const int8_t *xrow) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = b * U + u;
+            if (i < nmine) {
+                // step ks + S i is step ks + S (i - kb * BPB * U) of block kb = b / BPB
+                const int cl = 4 * (ks + S * (i - (b / BPB) * BPB * U)) + g;
+                const v4i *p = reinterpret_cast<const v4i *>(xrow + cl * 64);
+                const v4i bo[4] = {p[0], p[1], p[2], p[3]};
+                mfma_step_t(w[u], bo, a1, a4, a16);
+            }
+        }
+    };
+    auto next_block = [&](int kb) {
+        if (kb + 1 < nblocks) {  // uniform
+            store_block(kb + 1);
+            __syncthreads();
+        }
+    };
+    if constexpr (BPB == 2) {
+        for (int kb = 0; kb < nblocks; ++kb) {
+            if (kb + 1 < nblocks)
+                load_block(kb + 1);
+            const int8_t *xrow = xbuf + (kb & 1) * bufbytes + rt * BPITCH;
+            const int b = 2 * kb;
+            compute_batch(wa, b, xrow);
+            if (b + 2 < nb)
+                load_batch(wa, b + 2);
+            compute_batch(wb, b + 1, xrow);
+            if (b + 3 < nb)
+                load_batch(wb, b + 3);
+            next_block(kb);
+        }
+    } else {
+        // one batch per block: blocks alternate between the two register batches
+        auto one_block = [&](v4i (&w)[U], int kb) {
+            if (kb + 1 < nblocks)
+                load_block(kb + 1);
+            compute_batch(w, kb, xbuf + (kb & 1) * bufbytes + rt * BPITCH);
+            if (kb + 2 < nb)
+                load_batch(w, kb + 2);
+            next_block(kb);
+        };
+        for (int kb = 0; kb < nblocks; kb += 2) {
+            one_block(wa, kb);
+            if (kb + 1 < nblocks)
+                one_block(wb, kb + 1);
+        }
+    }
+
+    // 3. k-split sum (S > 1) and the epilogue, as in k_gemv_staged.
+    int part[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        part[v] = a1[v] + (a4[v] >> 2) + (a16[v] >> 4);
+    if constexpr (S > 1) {
+        if (ks != KE)
+            red[wave * 64 + lane] = make_int4(part[0], part[1], part[2], part[3]);
+        __syncthreads();
+        if (ks == KE) {
+#pragma unroll
+            for (int j = 0; j < KE; ++j) {
+                const int4 o = red[(wave - KE + j) * 64 + lane];
+                part[0] += o.x, part[1] += o.y, part[2] += o.z, part[3] += o.w;
+            }
+        }
+    }
+    if (ks == KE && r < M) {
+        const float sc[4] = {gam.x * sx_r, gam.y * sx_r, gam.z * sx_r, gam.w * sx_r};
+        const int64_t n0 = (int64_t)b16 * 16 + 4 * g;
+        if ((N & 3) == 0 && n0 < N && ((reinterpret_cast<uintptr_t>(Y) | reinterpret_cast<uintptr_t>(ACC)) & 15) == 0) {
+            const int4 acc = make_int4(part[0] - qs_r, part[1] - qs_r, part[2] - qs_r, part[3] - qs_r);
+            if (ACC)
+                *reinterpret_cast<int4 *>(ACC + (int64_t)r * N + n0) = acc;
+            if (Y)
+                *reinterpret_cast<float4 *>(Y + (int64_t)r * N + n0) =
+                    make_float4((float)acc.x * sc[0], (float)acc.y * sc[1], (float)acc.z * sc[2], (float)acc.w * sc[3]);
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t n = n0 + v;
+                if (n < N) {
+                    const int acc = part[v] - qs_r;
+                    if (ACC)
+                        ACC[(int64_t)r * N + n] = acc;
+                    if (Y)
+                        Y[(int64_t)r * N + n] = (float)acc * sc[v];
+                }
+            }
+        }
+    }
+}
+
 int pick_rb(int64_t N)
 {
     const int64_t nb16 = (N + 15) / 16;
@@ -1055,6 +1252,49 @@ hipError_t launch_staged_mt(const StagedPick &p, const uint4 *Wp, const float *w
     }
 }
 
+// Template arguments of the blocked kernel (k_gemv_blocked<S, U, BPB>): the staged kernel's
+// k-splits, then the largest batch U <= 4 and batches per block BPB <= 2 whose block
+// (BPB S U steps of M rows, M taken as 8 or 16) each thread stages in two 64-byte chunks
+// (M * 4 * BPB * S * U <= 1024 chunks); the two LDS buffers then hold at most 128 KB of rows.
+// A large U keeps the weight bytes in flight; the second batch per block halves the barriers.
+struct BlockedPick {
+    int s, u, bpb;
+};
+
+BlockedPick pick_blocked(int64_t M, int64_t N)
+{
+    const int s = pick_s(N);
+    const int64_t mcap = M <= 8 ? 8 : 16;
+    const int64_t chunks = 2 * kFusedWaves * 64;
+    int u = 4;
+    while (u > 1 && mcap * 4 * s * u > chunks)
+        --u;
+    return {s, u, mcap * 4 * 2 * s * u <= chunks ? 2 : 1};
+}
+
+size_t blocked_lds(int64_t M, int s, int u, int bpb)
+{
+    return (s > 1 ? kFusedWaves * 64 * 16 : 0) + 2 * (size_t)M * (size_t)(4 * bpb * s * u * 64 + kPitchPad);
+}
+
+template <int S, int U, int BPB>
+hipError_t launch_blocked_su(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq,
+                             const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
+                             int32_t *acc, hipStream_t s)
+{
+    constexpr int RBW = kFusedWaves / S;
+    const int64_t nb16 = (N + 15) / 16;
+    const dim3 grid((unsigned)((nb16 + RBW - 1) / RBW)), block(kFusedWaves * 64);
+    const size_t lds = blocked_lds(M, S, U, BPB);
+    if (row_scales)
+        hipLaunchKernelGGL((k_gemv_blocked<S, U, BPB, true>), grid, block, lds, s, Wp, w_scale, Xq, Y, acc, (int)M,
+                           (int)N, (int)K, sx, xsum);
+    else
+        hipLaunchKernelGGL((k_gemv_blocked<S, U, BPB, false>), grid, block, lds, s, Wp, w_scale, Xq, Y, acc, (int)M,
+                           (int)N, (int)K, sx, xsum);
+    return hipGetLastError();
+}
+
 // The direct kernel for one call: RB row blocks per workgroup, and for one row block the
 // double-buffered form with batches of U steps. One row block: two-step batches, two in
 // flight once a wave owns more than two steps. More row blocks: the single-batch kernel
@@ -1114,8 +1354,21 @@ hipError_t launch_gemv_staged(const uint4 *Wp, const float *w_scale, bool row_sc
                               const float *sx, const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y,
                               int32_t *acc, hipStream_t s)
 {
-    if (!gemv_staged_fits(M, N, K))
+    if (M < 1 || M > 16 || K < 1)
         return hipErrorInvalidValue;
+    if (!gemv_staged_fits(M, N, K)) {
+        // rows too long to stage whole: the blocked form (the picks below are all it takes)
+        const BlockedPick b = pick_blocked(M, N);
+        switch (b.s * 100 + b.u * 10 + b.bpb) {
+        case 142: return launch_blocked_su<1, 4, 2>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+        case 242: return launch_blocked_su<2, 4, 2>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+        case 442: return launch_blocked_su<4, 4, 2>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+        case 441: return launch_blocked_su<4, 4, 1>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+        case 841: return launch_blocked_su<8, 4, 1>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+        case 821: return launch_blocked_su<8, 2, 1>(Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     const StagedPick p = pick_staged(M, N, K);
     if (p.mt == 8)
         return launch_staged_mt<8>(p, Wp, w_scale, row_scales, Xq, sx, xsum, M, N, K, Y, acc, s);
@@ -1157,6 +1410,10 @@ int plan_linear_decode(int64_t M, int64_t N, int64_t K, bool row_scales, char *b
 
 int plan_gemv_staged(int64_t M, int64_t N, int64_t K, bool row_scales, char *buf, size_t len)
 {
+    if (!gemv_staged_fits(M, N, K)) {
+        const BlockedPick b = pick_blocked(M, N);
+        return snprintf(buf, len, "k_gemv_blocked<S=%d,U=%d,BPB=%d,ROWS=%d>", b.s, b.u, b.bpb, (int)row_scales);
+    }
     const StagedPick p = pick_staged(M, N, K);
     return snprintf(buf, len, "k_gemv_staged<MT=%d,S=%d,U=%d,ROWS=%d,CH=%d>", p.mt, p.s, p.u, (int)row_scales, p.ch);
 }

@@ -655,17 +655,62 @@ def test_gemv_staged(M, N, K):
     np.testing.assert_array_equal(Y1.cpu().numpy(), Y2.cpu().numpy())
 
 
+# Rows too long to stage whole (M * K rounded up to 256 above 128 KB): the blocked form,
+# which stages them in K-blocks of 2 S U steps. The k-splits S = 8, 4, 2, 1 (N) and token
+# capacities 8 and 16 (M) cover every (S, U) pick; K ragged, K spanning a partial last block,
+# and the 100B-class down shape at 5, 8 and 16 tokens.
+BLOCKED_CASES = [(16, 64, 8448), (16, 2560, 28672), (5, 8192, 28672), (8, 8192, 28672), (16, 8192, 28672),
+                 (9, 4096, 16000), (16, 20000, 8450), (12, 9000, 11008), (6, 4096, 22000), (16, 300, 131072)]
+
+
+@pytest.mark.parametrize("M,N,K", BLOCKED_CASES)
+def test_gemv_blocked(M, N, K):
+    """BT_GEMV_STAGED (and BT_GEMV_AUTO) on rows staged in K-blocks, against the oracle (all rows up
+    to 10000, else sampled) and bit-identical to the direct MFMA kernel."""
+    plan = bt.kernel_plan(bt.CALL_GEMV, M, N, K, bt.GEMV_STAGED)
+    note(f"gemv blocked M={M} N={N} K={K} plan={plan}")
+    assert plan.startswith("k_gemv_blocked") and plan == bt.kernel_plan(bt.CALL_GEMV, M, N, K)
+    W = synth.gaussian((N, K), 9880 + N + K, 0.02)
+    X = synth.gaussian((M, K), 9890 + M + K)
+    if M >= 3:
+        X[1] = 0.0
+    pw = gpu_pack(W)
+    q = gpu_quant(X)
+    Y1, acc1 = bt.ternary_gemv(pw, q, want_acc=True, algo=bt.GEMV_STAGED)
+    Y2, acc2 = bt.ternary_gemv(pw, q, want_acc=True, algo=bt.GEMV_MFMA)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc1.cpu().numpy(), acc2.cpu().numpy())
+    np.testing.assert_array_equal(Y1.cpu().numpy(), Y2.cpu().numpy())
+    # gamma is the whole matrix's; the codes and products of the compared rows
+    rows = np.arange(N) if N <= 10000 else np.unique(np.concatenate([np.arange(0, N, 97), [N - 1]]))
+    g = oracle.absmean(W)
+    Q, sx, _ = oracle.quant_act(X)
+    acc_ref = oracle.ternary_matmul(oracle.ternarize(W[rows], g), Q)
+    np.testing.assert_array_equal(acc1.cpu().numpy()[:, rows], acc_ref)
+    assert tol_ok(Y1.cpu().numpy()[:, rows], oracle.scale_epilogue(acc_ref, g, sx))
+
+
 def test_gemv_staged_limits_and_row_scales():
     note("gemv staged limits / row scales")
-    # 16 tokens x 8448 columns of int8 would need 132 KB of LDS: refused by the explicit
-    # choice, taken by the direct kernel under BT_GEMV_AUTO
+    # 16 tokens x 8448 columns of int8 would need 132 KB of LDS whole: the explicit staged
+    # choice and BT_GEMV_AUTO both take the blocked form
     W = synth.gaussian((64, 8448), 9900, 0.02)
     X = synth.gaussian((16, 8448), 9901)
     pw, q = gpu_pack(W), gpu_quant(X)
-    with pytest.raises(bt.BTError):
-        bt.ternary_gemv(pw, q, algo=bt.GEMV_STAGED)
     ref = oracle_layer(W, X)
+    check_product(pw, q, ref, 16, 64, bt.ternary_gemv, algo=bt.GEMV_STAGED)
     check_product(pw, q, ref, 16, 64, bt.ternary_gemv, algo=bt.GEMV_AUTO)
+    # the blocked form with row scales
+    N, K, groups = 768, 9000, [640, 64, 64]
+    W = synth.gaussian((N, K), 9904, 0.02)
+    W[640:704] *= np.float32(5.0)
+    X = synth.gaussian((16, K), 9905)
+    ref = oracle.linear_rows(W, X, groups)
+    pw = bt.pack_weights_rows(to_dev(W), groups)
+    Y, acc = bt.ternary_gemv(pw, bt.quant_act(to_dev(X)), want_acc=True, algo=bt.GEMV_STAGED)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    assert tol_ok(Y.cpu().numpy(), ref["Y"])
     # row scales
     N, K, groups = 768, 700, [640, 64, 64]
     W = synth.gaussian((N, K), 9902, 0.02)
