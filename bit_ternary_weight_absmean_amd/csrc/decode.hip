@@ -313,16 +313,19 @@ __global__ __launch_bounds__(kDirectWaves * 64) void k_gemv_direct_db(
         load_batch(w0, x0, 0);
         load_batch(w1, x1, 1);
     }
-    for (int b = 0; b < nb; b += 2) {
+    // Pairs of batches while the next pair exists, its loads unconditional (at clamped valid
+    // addresses: at most one batch past the last), then the last pair with no loads. A load
+    // under a branch would leave the compiler unable to count the loads issued after a batch,
+    // and its waits for that batch would then cover the batch behind it too.
+    int b = 0;
+    for (; b + 2 < nb; b += 2) {
         compute_batch(w0, x0, b);
-        if (b + 2 < nb)
-            load_batch(w0, x0, b + 2);
-        if (b + 1 < nb) {
-            compute_batch(w1, x1, b + 1);
-            if (b + 3 < nb)
-                load_batch(w1, x1, b + 3);
-        }
+        load_batch(w0, x0, b + 2);
+        compute_batch(w1, x1, b + 1);
+        load_batch(w1, x1, b + 3);
     }
+    compute_batch(w0, x0, b);
+    compute_batch(w1, x1, b + 1);
 #pragma unroll
     for (int k = 0; k < RB; ++k)
 #pragma unroll
@@ -608,16 +611,16 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
                 }
             }
         };
-        for (int b = 0; b < nb; b += 2) {
+        // Batch pairs with unconditional loads, then the last pair (as in k_gemv_direct_db).
+        int b = 0;
+        for (; b + 2 < nb; b += 2) {
             compute_batch(wa, b);
-            if (b + 2 < nb)
-                load_batch(wa, b + 2);
-            if (b + 1 < nb) {
-                compute_batch(wb, b + 1);
-                if (b + 3 < nb)
-                    load_batch(wb, b + 3);
-            }
+            load_batch(wa, b + 2);
+            compute_batch(wb, b + 1);
+            load_batch(wb, b + 3);
         }
+        compute_batch(wa, b);
+        compute_batch(wb, b + 1);
     }
 
     // 6. Combine the k-splits of each block (S > 1) and write y / acc. Lane (g, r) holds
@@ -804,16 +807,16 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv_staged(
             }
         }
     };
-    for (int b = 0; b < nb; b += 2) {
+    // Batch pairs with unconditional loads, then the last pair (as in k_gemv_direct_db).
+    int b = 0;
+    for (; b + 2 < nb; b += 2) {
         compute_batch(wa, b);
-        if (b + 2 < nb)
-            load_batch(wa, b + 2);
-        if (b + 1 < nb) {
-            compute_batch(wb, b + 1);
-            if (b + 3 < nb)
-                load_batch(wb, b + 3);
-        }
+        load_batch(wa, b + 2);
+        compute_batch(wb, b + 1);
+        load_batch(wb, b + 3);
     }
+    compute_batch(wa, b);
+    compute_batch(wb, b + 1);
 
     // 5. k-split sum (S > 1) and the epilogue; lane (g, r) holds rows 4g + v for token r.
     int part[4];
@@ -981,28 +984,27 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv_blocked(
             __syncthreads();
         }
     };
+    // Every load below is unconditional, at clamped valid addresses (past the last block or
+    // batch they re-read the row's last chunk, which stays cached): a load under a branch
+    // would leave the compiler unable to count the loads issued after a batch, and every
+    // wait for that batch would then wait for the next block's activations as well.
     if constexpr (BPB == 2) {
         for (int kb = 0; kb < nblocks; ++kb) {
-            if (kb + 1 < nblocks)
-                load_block(kb + 1);
+            load_block(kb + 1);
             const int8_t *xrow = xbuf + (kb & 1) * bufbytes + rt * BPITCH;
             const int b = 2 * kb;
             compute_batch(wa, b, xrow);
-            if (b + 2 < nb)
-                load_batch(wa, b + 2);
+            load_batch(wa, b + 2);
             compute_batch(wb, b + 1, xrow);
-            if (b + 3 < nb)
-                load_batch(wb, b + 3);
+            load_batch(wb, b + 3);
             next_block(kb);
         }
     } else {
         // one batch per block: blocks alternate between the two register batches
         auto one_block = [&](v4i (&w)[U], int kb) {
-            if (kb + 1 < nblocks)
-                load_block(kb + 1);
+            load_block(kb + 1);
             compute_batch(w, kb, xbuf + (kb & 1) * bufbytes + rt * BPITCH);
-            if (kb + 2 < nb)
-                load_batch(w, kb + 2);
+            load_batch(w, kb + 2);
             next_block(kb);
         };
         for (int kb = 0; kb < nblocks; kb += 2) {
