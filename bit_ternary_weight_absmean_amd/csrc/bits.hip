@@ -147,15 +147,26 @@ __global__ __launch_bounds__(kBitWaves * 64) void k_gemv_bits(const uint32_t *__
 #pragma unroll
     for (int m = 0; m < MT; ++m)
         differ[m] = 0;
-    // kBitUnroll chunks per wave in flight: the loads of a batch (at clamped, valid
-    // chunks) are issued before any of them is used.
-    for (int c0 = wave; c0 < KC; c0 += kBitWaves * kBitUnroll) {
-        uint32_t wv[kBitUnroll];
+    // U chunks per wave in flight: every load of a batch -- the weight words, then the
+    // token words -- is issued, unconditionally at clamped valid addresses (chunks past KC
+    // re-read the last one, tokens past M re-read token M - 1), before any is used; the
+    // arithmetic is guarded instead. A load under a branch would make each wait cover every
+    // load issued before it, one round trip per chunk.
+    constexpr int U = MT <= 4 ? kBitUnroll : kBitUnroll / 2;
+    for (int c0 = wave; c0 < KC; c0 += kBitWaves * U) {
+        uint32_t wv[U], xv[U][MT];
 #pragma unroll
-        for (int u = 0; u < kBitUnroll; ++u)
+        for (int u = 0; u < U; ++u)
             wv[u] = wrow[(int64_t)min(c0 + u * kBitWaves, KC - 1) * 256];
 #pragma unroll
-        for (int u = 0; u < kBitUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
+            const int cc = min(c0 + u * kBitWaves, KC - 1);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                xv[u][m] = Xb[(int64_t)min(m, M - 1) * xwords + 4 * cc + j];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
             const int c = c0 + u * kBitWaves;
             if (c < KC) {  // wave-uniform
                 const uint32_t w = wv[u];
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(kBitWaves * 64) void k_gemv_bits(const uint32_t *__
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     if (m < M) {
-                        const uint32_t d = neg ^ Xb[(int64_t)m * xwords + 4 * c + j];
+                        const uint32_t d = neg ^ xv[u][m];
                         differ[m] += __builtin_popcount(TERNARY ? (d & mag) : d);
                     }
                 }
