@@ -26,6 +26,7 @@ namespace {
 constexpr int kLutWaves = 4;
 constexpr int kLutRows = 16;   // weight rows per workgroup: lane = 4 * row + word
 constexpr int kLutUnroll = 4;  // chunks in flight per wave
+constexpr int kLutBuild = 8;   // tables whose activation bytes each thread loads together
 
 template <int CTRL>
 __device__ inline int lut_dpp(int v)
@@ -49,22 +50,38 @@ __global__ __launch_bounds__(kLutWaves * 64) void k_gemv_lut(const uint32_t *__r
 
     // 1. The tables: thread t fills the tables (g, p) = t, t + 256, ... (16 entries,
     //    two 16-byte LDS stores each). Xq rows are zero past K up to a multiple of 256,
-    //    so every k read here lies in the row.
-    for (int pair = tid; pair < KG * 8; pair += kLutWaves * 64) {
-        const int g = pair >> 3, p = pair & 7;
-        const int k0 = 16 * g + (p >> 1) + 8 * (p & 1);
-        const int q0 = Xq[k0], q1 = Xq[k0 + 4];
-        uint32_t packed[8];
+    //    so every k read here lies in the row. The two activation bytes of kLutBuild
+    //    tables are loaded together (unconditionally, at clamped tables) before any is
+    //    built: loaded one table at a time, every table waited a round trip of its own.
+    constexpr int T = kLutWaves * 64;
+    const int npairs = KG * 8;
+    for (int base = tid; base < npairs; base += T * kLutBuild) {
+        int q0[kLutBuild], q1[kLutBuild];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int v0 = 2 * i, v1 = 2 * i + 1;
-            const int e0 = (v0 & 3) * q0 + (v0 >> 2) * q1;
-            const int e1 = (v1 & 3) * q0 + (v1 >> 2) * q1;
-            packed[i] = ((uint32_t)e0 & 0xFFFFu) | ((uint32_t)e1 << 16);
+        for (int i = 0; i < kLutBuild; ++i) {
+            const int pair = min(base + i * T, npairs - 1);
+            const int g = pair >> 3, p = pair & 7;
+            const int k0 = 16 * g + (p >> 1) + 8 * (p & 1);
+            q0[i] = Xq[k0];
+            q1[i] = Xq[k0 + 4];
         }
-        uint4 *dst = reinterpret_cast<uint4 *>(smem + (size_t)pair * 32);
-        dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+#pragma unroll
+        for (int i = 0; i < kLutBuild; ++i) {
+            const int pair = base + i * T;
+            if (pair < npairs) {
+                uint32_t packed[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int v0 = 2 * e, v1 = 2 * e + 1;
+                    const int e0 = (v0 & 3) * q0[i] + (v0 >> 2) * q1[i];
+                    const int e1 = (v1 & 3) * q0[i] + (v1 >> 2) * q1[i];
+                    packed[e] = ((uint32_t)e0 & 0xFFFFu) | ((uint32_t)e1 << 16);
+                }
+                uint4 *dst = reinterpret_cast<uint4 *>(smem + (size_t)pair * 32);
+                dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+                dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+            }
+        }
     }
     __syncthreads();
 
