@@ -920,7 +920,8 @@ def summarize_trace(args):
                      f"| {len(gp)} | {statistics.mean(gp) if gp else float('nan'):.3f} | "
                      f"{statistics.median(gp) if gp else float('nan'):.3f} |")
     # every product kernel of the workload together
-    for kname in ("k_linear_decode", "k_gemv_staged", "k_gemv_blocked", "k_gemv_direct", "k_gemm"):
+    for kname in ("k_linear_decode", "k_gemv_staged", "k_gemv_blocked", "k_gemv_direct", "k_gemv_lut", "k_gemv_bits",
+                  "k_gemm"):
         d = [x for (n, _, _), e in per.items() if kname in n for x in e["dur"]]
         gp = [x for (n, _, _), e in per.items() if kname in n for x in e["gap"]]
         if d:
