@@ -592,7 +592,9 @@ def run_onebit(args):
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": cpu,
-        "detail": {"dominant_kernel": "k_gemv_bits", "kernel_avg_us": round(prod_us, 3),
+        "detail": {"dominant_kernel": "k_gemv_bits", "launch_interval_us": round(prod_us, 3),
+                   "launch_interval_note": "the GEMV launches of one step replayed as a HIP graph (binarize "
+                                           "launches left out), timed with HIP events, divided by the launches",
                    "algorithmic_bytes_per_launch": round(prod_bytes / n_prod),
                    "gemv_GOPS": round(ops / (ms_prod * 1e-3) / 1e9, 1),
                    "resident_packed_bytes": sum(p.data.numel() for row in packed for p in row)},
