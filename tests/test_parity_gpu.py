@@ -490,6 +490,31 @@ def test_linear_fused(M, N, K):
     np.testing.assert_array_equal(Y.cpu().numpy(), Ys.cpu().numpy())
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 3840, 2560), (4, 300, 1000), (2, 600, 6912), (8, 500, 2560)])
+def test_linear_misaligned_input(M, N, K):
+    """Token rows at a 4-byte (not 16-byte) offset with K % 4 == 0: the fused kernel then reads
+    them with scalar loads instead of its register path, the unfused route's quantizer likewise.
+    Against the oracle, and bit-identical to the same call on an aligned copy (both entry points)."""
+    note(f"linear misaligned input M={M} N={N} K={K}")
+    W = synth.gaussian((N, K), 9400 + N + K, 0.02)
+    X = synth.gaussian((M, K), 9900 + M + K)
+    ref = oracle_layer(W, X)
+    pw = gpu_pack(W)
+    big = torch.zeros(X.size + 1, dtype=torch.float32, device=DEV)
+    big[1:] = to_dev(X.ravel())
+    Xd = big[1:].view(M, K)
+    assert Xd.data_ptr() % 16 == 4
+    Y, acc = bt.linear(Xd, pw, want_acc=True)
+    Ys, accs = bt.linear_static(Xd, pw, want_acc=True)
+    Ya, acca = bt.linear(to_dev(X), pw, want_acc=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    assert tol_ok(Y.cpu().numpy(), ref["Y"])
+    for y, a in ((Ys, accs), (Ya, acca)):
+        np.testing.assert_array_equal(a.cpu().numpy(), ref["acc"])
+        np.testing.assert_array_equal(f32_bits(y.cpu().numpy()), f32_bits(Y.cpu().numpy()))
+
+
 @pytest.mark.parametrize("M,N,K", [(16, 512, 8192), (16, 600, 28672), (40, 300, 700), (300, 257, 1000),
                                    (5, 200, 700), (8, 64, 64), (16, 300, 517), (16, 1000, 2560),
                                    (8, 4096, 4096), (4, 300, 11008)])
