@@ -63,6 +63,7 @@ KERNEL_SOURCES = {
     "k_gemv_dot4": ["gemv.hip", "bt_internal.h"],
     "k_gemv_lut": ["lut.hip", "bt_internal.h"],
     "k_gemm": ["gemm.hip", "bt_internal.h"],
+    "k_gemm_ks": ["gemm.hip", "bt_internal.h"],
 }
 
 
@@ -251,8 +252,9 @@ def run_gpu(args, spec):
         _, N, K = shapes[j]
         if fused_j[j]:
             return "k_linear_decode"
-        if gemm:
-            return "k_gemm"
+        if gemm:  # the small-M form where the GEMM takes it (few tiles), else k_gemm
+            small = bt.kernel_plan(bt.CALL_GEMM_WS, M, N, K).startswith("k_gemm_ks")
+            return "k_gemm_ks" if small else "k_gemm"
         if args.gemv_algo in ("auto", "staged"):  # BT_GEMV_AUTO takes the staged forms, as bt_ternary_linear
             return staged_name(N, K)
         return names[args.gemv_algo]
@@ -1166,7 +1168,7 @@ def main():
                                  "shape, else bt_quant_act + bt_ternary_gemv)" if g["fused_any"]
                             else ("per matrix: bt_quant_act + " if args.split else
                                   "per matrix: bt_ternary_linear = bt_quant_act + ") +
-                            ("bt_ternary_gemm_ws" if g["kernel"] == "k_gemm" else "bt_ternary_gemv"))},
+                            ("bt_ternary_gemm_ws" if "k_gemm" in g["kernel"] else "bt_ternary_gemv"))},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": detail,

@@ -39,6 +39,9 @@
 //    rows walked weight-tile column by column): the workgroups resident on an XCD then
 //    share 8 activation panels and a few weight panels in its L2, instead of streaming a
 //    different weight panel each from HBM.
+//  * products with too few tiles to fill the CUs (a few hundred tokens) take a second
+//    kernel, k_gemm_ks: 64 x 64 tiles whose k-steps four waves of a workgroup share, with
+//    the partial tiles summed in LDS (see its comment below).
 #include <algorithm>
 #include <type_traits>
 
@@ -475,6 +478,218 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
     }
 }
 
+// ------------------------------------------------------------ small-M form
+// For products whose 64 x 256 tiles would leave most CUs idle (a few hundred tokens against
+// a few thousand rows): 64 x 64 output tiles, one per workgroup of four waves, with the
+// tile's 128-k steps split four ways inside the workgroup. Wave w streams a contiguous
+// share of the steps through NS stages of its own (each stage: the step's 64 x 128
+// activation block and 64 x 32 packed weight block, brought by direct loads in k_gemm's
+// LDS layouts), so the main loop has no workgroup barrier: a wave's own waits order its
+// loads and its reads. The four partial tiles then meet in LDS, and wave w finishes token
+// rows 16 w .. 16 w + 15 of the tile. Against k_gemm's split-K form the partial tiles
+// never leave the CU, and every tile gets a whole CU's four SIMDs.
+constexpr int kKsWaves = 4;
+constexpr int kKsA = 64 * kBK;         // activation block of a step: 64 rows x 128 bytes
+constexpr int kKsB = 64 * kBK / 4;     // packed weight block of a step: 64 rows x 32 bytes
+constexpr int kKsStage = kKsA + kKsB;  // one wave's stage: 10 KB
+constexpr int kKsLoads = kKsA / 1024 + kKsB / 1024;  // direct loads per wave and step
+
+template <int NS>
+__global__ __launch_bounds__(kKsWaves * 64) void k_gemm_ks(
+    const uint4 *__restrict__ Wp, const float *__restrict__ w_scale, const int8_t *__restrict__ Xq, int64_t ldq,
+    const float *__restrict__ sx, const int32_t *__restrict__ xsum, int64_t M, int64_t N, int KC, int tiles_m,
+    int tiles, int per_xcd, float *__restrict__ Y, int32_t *__restrict__ ACC, int rows)
+{
+    static_assert(NS == 3, "three stages (the ring below is written for three)");
+    // One array per ring stage, each holding the four waves' copies of that stage (as in
+    // k_gemm: distinct objects let the compiler tell which stage a direct load writes).
+    __shared__ __attribute__((aligned(1024))) int8_t lds0[kKsWaves * kKsStage];
+    __shared__ __attribute__((aligned(1024))) int8_t lds1[kKsWaves * kKsStage];
+    __shared__ __attribute__((aligned(1024))) int8_t lds2[kKsWaves * kKsStage];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int g = lane >> 4, r = lane & 15;
+
+    // Workgroup b runs on XCD b % 8; each XCD takes a contiguous run of tiles, token tiles
+    // fastest, so the tiles that share a weight block share that XCD's L2.
+    const int b = blockIdx.x;
+    const int t = (b % kXcds) * per_xcd + b / kXcds;
+    if (t >= tiles)
+        return;
+    const int tm = t % tiles_m, tn = t / tiles_m;
+    const int64_t m0 = (int64_t)tm * 64;
+    const int64_t n0 = (int64_t)tn * 64;
+
+    // This wave's steps: [step0, step0 + nsteps) of the tile's ceil(KC / 2).
+    const int nsteps_all = (KC + 1) / 2;
+    const int per = (nsteps_all + kKsWaves - 1) / kKsWaves;
+    const int step0 = min(wave * per, nsteps_all);
+    const int nsteps = min(per, nsteps_all - step0);
+    const int last = nsteps - 1;
+    const int KCl = KC - 2 * step0;  // 64-k chunks from the wave's first step on
+
+    // Direct loads of one step. Activation block q (16-row tile q / 2, half q % 2): lane L
+    // brings row 8 (q % 2) + L / 8 of the tile, the piece slot L % 8 of that row holds
+    // (slot ^ row ^ half); rows past M read row M - 1. Weight block gq: chunk gq of the step,
+    // lane L bringing row L's 16 bytes; chunks past K read the last chunk (against zero
+    // activations: activation rows are zero-padded to a multiple of 256 bytes).
+    const int8_t *xbase = Xq + m0 * ldq + (int64_t)step0 * kBK;
+    uint32_t aoff[kKsA / 1024];
+#pragma unroll
+    for (int q = 0; q < kKsA / 1024; ++q) {
+        const int at = q >> 1, h = q & 1;
+        const int rho = lane >> 3, slot = lane & 7;
+        const int64_t m = min(m0 + at * 16 + 8 * h + rho, M - 1);
+        aoff[q] = (uint32_t)((m - m0) * ldq + (slot ^ rho ^ h) * 16);
+    }
+    const int8_t *wrow = reinterpret_cast<const int8_t *>(Wp) + (int64_t)tn * KC * 1024 + (int64_t)step0 * 2048 +
+                         lane * 16;
+    const int wslot = wave * kKsStage;
+    auto issue = [&](int st, int8_t *stage) {
+        int8_t *sdst = stage + wslot;
+        const int8_t *xs = xbase + (int64_t)st * kBK;
+#pragma unroll
+        for (int q = 0; q < kKsA / 1024; ++q)
+            __builtin_amdgcn_global_load_lds((global_void *)(xs + aoff[q]), (lds_void *)(sdst + q * 1024), 16, 0, 0);
+#pragma unroll
+        for (int gq = 0; gq < 2; ++gq)
+            __builtin_amdgcn_global_load_lds((global_void *)(wrow + (int64_t)min(2 * st + gq, KCl - 1) * 1024),
+                                             (lds_void *)(sdst + kKsA + gq * 1024), 16, 0, 0);
+    };
+
+    v4i acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[a][i] = v4i{0, 0, 0, 0};
+
+    // Operand reads within the wave's stage, as in k_gemm (one wave tile of 4 x 4 MFMA
+    // tiles): activation row r of 16-row tile a, piece 2 g + j; weight words 2 (g & 1), +1
+    // of chunk g / 2 of row 16 i + r.
+    const int hr = r >> 3, rho_r = r & 7, c = rho_r ^ hr;
+    const int a_row = wslot + hr * 1024 + rho_r * 128;
+    const int a_off0 = a_row + ((2 * g) ^ c) * 16;
+    const int a_off1 = a_row + ((2 * g + 1) ^ c) * 16;
+    const int b_off = wslot + kKsA + (g >> 1) * 1024 + r * 16 + 8 * (g & 1);
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    v4i fa0[4], fa1[4];
+    v2u fb[4], fbn[4];
+    auto read_a = [&](const int8_t *sp, int off, v4i (&fa)[4]) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+            fa[a] = *reinterpret_cast<const v4i *>(sp + off + a * 2048);
+    };
+    auto read_b = [&](const int8_t *sp, v2u (&f)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            f[i] = *reinterpret_cast<const v2u *>(sp + b_off + i * 256);
+    };
+    auto mma = [&](const v4i (&fa)[4], const v2u (&f)[4], int j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v4i bop = unpack_word(f[i][j]);
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                acc[a][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[a], bop, acc[a][i], 0, 0, 0);
+        }
+    };
+    // Before refilling a stage: step st + 1's loads landed (at most one step of loads still
+    // outstanding) and this wave's reads of the stage returned (lgkmcnt(0)).
+    constexpr int kWaitStep = vmcnt_imm((NS - 2) * kKsLoads) & ~(0xF << 8);
+    auto step = [&](int8_t *sp, int8_t *sn, int st) {
+        read_a(sp, a_off1, fa1);
+        mma(fa0, fb, 0);
+        __builtin_amdgcn_s_waitcnt(kWaitStep);
+        asm volatile("" ::: "memory");
+        issue(min(st + NS, last), sp);
+        read_a(sn, a_off0, fa0);
+        read_b(sn, fbn);
+        mma(fa1, fb, 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fb[i] = fbn[i];
+    };
+    if (nsteps > 0) {
+        issue(0, lds0);
+        issue(min(1, last), lds1);
+        issue(min(2, last), lds2);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * kKsLoads));
+        asm volatile("" ::: "memory");
+        read_a(lds0, a_off0, fa0);
+        read_b(lds0, fb);
+        int st = 0;
+        for (; st + NS <= nsteps; st += NS) {
+            step(lds0, lds1, st);
+            step(lds1, lds2, st + 1);
+            step(lds2, lds0, st + 2);
+        }
+        if (st < nsteps)
+            step(lds0, lds1, st);
+        if (st + 1 < nsteps)
+            step(lds1, lds2, st + 1);
+    }
+    // The trailing (clamped, unused) loads retire, then every wave is done with the rings.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+
+    // Partial tiles through LDS: wave w sends token tile a (acc[a][*]) to wave a, into slot
+    // (w - a - 1) mod 4 of a's area (48 KB in all: tiles 0, 1 in lds0, 2, 3 in lds1).
+    auto area = [&](int a) -> int8_t * { return (a < 2 ? lds0 : lds1) + (a & 1) * (3 * 4 * 64 * 16); };
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        if (a == wave)
+            continue;
+        const int s = (wave - a - 1) & 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<v4i *>(area(a) + ((s * 4 + i) * 64 + lane) * 16) = acc[a][i];
+    }
+    __syncthreads();
+    v4i d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        d[i] = acc[0][i];
+#pragma unroll
+        for (int a = 1; a < 4; ++a)
+            if (a == wave)
+                d[i] = acc[a][i];
+    }
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            d[i] += *reinterpret_cast<const v4i *>(area(wave) + ((s * 4 + i) * 64 + lane) * 16);
+
+    // Epilogue of token tile `wave`: lane (g, r) holds tokens 16 wave + 4 g + v, row 16 i + r.
+    int32_t xs_v[4];
+    float sx_v[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t m = min(m0 + 16 * wave + 4 * g + v, M - 1);
+        xs_v[v] = xsum[m];
+        sx_v[v] = sx[m];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t n = n0 + 16 * i + r;
+        const float gam = w_scale[rows ? min(n, N - 1) : 0];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t m = m0 + 16 * wave + 4 * g + v;
+            if (m < M && n < N) {
+                const int32_t dv = d[i][v] - xs_v[v];
+                if (ACC)
+                    __builtin_nontemporal_store(dv, ACC + m * N + n);
+                if (Y)
+                    __builtin_nontemporal_store((float)dv * (gam * sx_v[v]), Y + m * N + n);
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int NS, int WPE, bool SPLITK>
 hipError_t launch_t(const uint4 *Wp, const float *w_scale, bool row_scales, const int8_t *Xq, int64_t ldq, const float *sx,
                     const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, char *partials,
@@ -517,9 +732,21 @@ int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + kBM - 1) / kBM) * ((N + 
 //  * Otherwise every tile split in 2-4 (full = 0): it pays when the tiles alone leave most
 //    of the 768 workgroup slots (three per CU) empty and every split keeps enough steps to
 //    amortize its prologue, epilogue and the partial-tile hand-off through memory.
+// The small-M form (k_gemm_ks): at least four 128-k steps (one per wave), and few enough
+// 64 x 64 tiles for one workgroup per CU at a time. Measured on the 2B prefill shapes:
+// M = 256 QKV 12.6 -> 10.0 us, O 12.1 -> 9.9, down 16.5 -> 14.9 against the split-K form
+// (step 2.07 -> 1.91 ms); at M = 512 (320-480 tiles, two rounds) it was 5-35% slower.
+static bool gemm_small_form(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t tiles64 = ((M + 63) / 64) * ((N + 63) / 64);
+    return M > 0 && N > 0 && K >= 4 * 128 && tiles64 <= kCUs;
+}
+
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K)
 {
     const int64_t tiles = gemm_tiles(M, N);
+    if (gemm_small_form(M, N, K))
+        return {tiles, 1};  // no split: the small form sums its k-shares inside the workgroup
     const int64_t steps = ((K + 63) / 64 + 1) / 2;
     const int64_t r = tiles % kCUs;
     if (tiles >= kCUs && r > 0 && r <= kCUs / 2) {
@@ -549,8 +776,18 @@ hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, bool row_scales, c
                        const int32_t *xsum, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, void *workspace,
                        size_t workspace_bytes, hipStream_t s)
 {
-    // 64 x 256 blocks of 4 waves, three workgroups per CU (3-stage ring, 48 KB of LDS
-    // each): with three waves per SIMD one wave's LDS reads, unpacking and barrier wait
+    // Few tiles (gemm_small_form): 64 x 64 tiles with the k-steps split over a workgroup's
+    // four waves; needs no workspace.
+    if (gemm_small_form(M, N, K)) {
+        const int64_t tiles_m = (M + 63) / 64, tiles64 = tiles_m * ((N + 63) / 64);
+        const int per_xcd = (int)((tiles64 + kXcds - 1) / kXcds);
+        hipLaunchKernelGGL((k_gemm_ks<3>), dim3((unsigned)(per_xcd * kXcds)), dim3(kKsWaves * 64), 0, s, Wp, w_scale,
+                           Xq, ldq, sx, xsum, M, N, (int)((K + 63) / 64), (int)tiles_m, (int)tiles64, per_xcd, Y, acc,
+                           row_scales ? 1 : 0);
+        return hipGetLastError();
+    }
+    // Otherwise 64 x 256 blocks of 4 waves, three workgroups per CU (3-stage ring, 48 KB of
+    // LDS each): with three waves per SIMD one wave's LDS reads, unpacking and barrier wait
     // hide under the others' MFMAs. Measured on the 2B-class prefill shapes against
     // 128 x 256 blocks of 8 waves, 64 x 128 blocks of 2 waves, wave tiles of 32 and 128
     // tokens and two workgroups per CU with a 4-stage ring.
@@ -568,6 +805,8 @@ hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, bool row_scales, c
 
 int plan_gemm(int64_t M, int64_t N, int64_t K, bool row_scales, bool split_workspace, char *buf, size_t len)
 {
+    if (gemm_small_form(M, N, K))
+        return snprintf(buf, len, "k_gemm_ks<NS=3,ROWS=%d>", (int)row_scales);
     const GemmPlan pl = gemm_plan(M, N, K);
     const int64_t tiles = gemm_tiles(M, N);
     if (!split_workspace || pl.nsplit == 1)

@@ -159,9 +159,13 @@ def test_gemv_small(M, N, K, algo):
 
 
 # (257, 516, 700): ragged 64 x 256 tiles in both dimensions with both outputs;
-# (1024, 8448, 512): 528 tiles, more than one round of workgroups.
+# (1024, 8448, 512): 528 tiles, more than one round of workgroups. K >= 512 with at most
+# 256 tiles of 64 x 64 takes the small-M form (k_gemm_ks): (300, 200, 517), (64, 1000, 2560),
+# (257, 516, 700), and its k-share edges: 4 steps (one per wave), 5 steps of 9 chunks
+# (shares 2, 2, 1, 0), 5 whole steps, and exactly 256 tiles.
 GEMM_SMALL = [(1, 64, 64), (17, 100, 300), (128, 512, 256), (129, 130, 129), (300, 200, 517), (64, 1000, 2560),
-              (257, 516, 700), (1024, 8448, 512)]
+              (257, 516, 700), (1024, 8448, 512), (64, 64, 512), (200, 700, 513), (100, 130, 640),
+              (256, 4096, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SMALL)
@@ -255,8 +259,9 @@ def test_100b_down_decode_m16():
 
 
 # Split-K route (bt_ternary_gemm_ws): shapes chosen so that the split heuristic picks
-# 4, 3 and 2 workgroups for every tile, ragged in M, N and K.
-SPLIT_SHAPES = [(100, 2500, 6900, 4), (70, 600, 2500, 3), (65, 300, 1600, 2)]
+# 4, 3 and 2 workgroups for every tile, ragged in M, N and K (more 64 x 64 tiles than CUs,
+# so the small-M form does not take them).
+SPLIT_SHAPES = [(520, 2500, 6900, 4), (300, 3500, 2600, 3), (280, 4500, 1700, 2)]
 
 
 def split_of(M, N, K):
@@ -267,9 +272,15 @@ def split_of(M, N, K):
 def counters_zero(ws, M, N, K):
     """The arrival counters of the split tiles (the workspace's leading words) are zero."""
     full, splits = bt.gemm_split_plan(M, N, K)
+    if splits == 1:
+        return ws is None  # no split: no workspace either
     tiles = -(-M // 64) * -(-N // 256)
-    n = tiles - full if splits > 1 else 0
-    return bool((ws[: 4 * n].view(torch.int32) == 0).all())
+    return bool((ws[: 4 * (tiles - full)].view(torch.int32) == 0).all())
+
+
+def sampled_rows(M, step=29):
+    """Token rows in every 64-token tile row, the last row included."""
+    return np.concatenate([np.arange(3, M, step), [M - 1]])
 
 
 @pytest.mark.parametrize("M,N,K,S", SPLIT_SHAPES)
@@ -278,11 +289,18 @@ def test_gemm_split_k(M, N, K, S):
     assert bt.gemm_split_plan(M, N, K) == (0, S)
     W = synth.gaussian((N, K), 9150 + N, 0.02)
     X = synth.gaussian((M, K), 9650 + M)
-    ref = oracle_layer(W, X)
+    g = oracle.absmean(W)
+    T = oracle.ternarize(W, g)
+    Q, s, qs = oracle.quant_act(X)
+    rows = sampled_rows(M)
+    acc_ref = oracle.ternary_matmul(T, Q[rows])
     pw, q = gpu_pack(W), gpu_quant(X)
     ws = bt.gemm_workspace(M, N, K, DEV)
     for _ in range(2):  # the second call relies on the first leaving the counters at zero
-        check_product(pw, q, ref, M, N, bt.ternary_gemm, workspace=ws)
+        Y, acc = bt.ternary_gemm(pw, q, want_acc=True, workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy()[rows], acc_ref)
+        assert tol_ok(Y.cpu().numpy()[rows], oracle.scale_epilogue(acc_ref, g, s[rows]))
         assert counters_zero(ws, M, N, K)
     # bit-identical to the unsplit route
     Y1, a1 = bt.ternary_gemm(pw, q, want_acc=True)
@@ -323,7 +341,7 @@ def test_gemm_tail_split(M, N, K, full, S):
 
 
 def test_gemm_split_k_small_workspace_falls_back():
-    M, N, K = 100, 2500, 6900
+    M, N, K = 300, 3500, 2600
     note(f"gemm split-K short workspace M={M} N={N} K={K}")
     W = synth.gaussian((N, K), 9151, 0.02)
     X = synth.gaussian((M, K), 9651)
@@ -336,14 +354,15 @@ def test_gemm_split_k_small_workspace_falls_back():
     np.testing.assert_array_equal(f32_bits(Y1.cpu().numpy()), f32_bits(Y2.cpu().numpy()))
 
 
-@pytest.mark.parametrize("M,j", [(256, 0), (256, 1), (256, 3), (2048, 3)])
-def test_2b_prefill_split_shapes(M, j):
-    """The 2B prefill shapes that split (M=256: QKV, O, down; M=2048: down), in the
-    launch configuration the benchmark times: sampled rows against the oracle, every
-    output bit-identical to the unsplit route."""
+@pytest.mark.parametrize("M,j,kernel", [(256, 0, "k_gemm_ks"), (256, 1, "k_gemm_ks"), (256, 3, "k_gemm_ks"),
+                                        (2048, 3, "k_gemm<SPLITK=1")])
+def test_2b_prefill_routed_shapes(M, j, kernel):
+    """The 2B prefill shapes that take the small-M form (M=256: QKV, O, down) or split their
+    last round (M=2048: down), in the launch configuration the benchmark times: sampled rows
+    against the oracle, every output bit-identical to the call without a workspace."""
     name, N, K = synth.SHAPES_2B[j]
-    note(f"2B prefill split M={M} {name}")
-    assert split_of(M, N, K) > 1
+    note(f"2B prefill M={M} {name} ({kernel})")
+    assert bt.kernel_plan(bt.CALL_GEMM_WS, M, N, K).startswith(kernel)
     W = synth.layer_weight(synth.CFG_2B_PREFILL, 0, j, N, K)
     X = synth.layer_activation(synth.CFG_2B_PREFILL, j, M, K)
     g = oracle.absmean(W)
@@ -560,18 +579,23 @@ def test_linear_tail_split_garbage_workspace():
 def test_linear_split_k_garbage_workspace():
     """bt_ternary_linear on a shape whose GEMM splits K, with a workspace full of garbage:
     the call initializes everything it reads (the quantizer zero-fills the counters)."""
-    M, N, K = 100, 2500, 6900
+    M, N, K = 300, 3500, 2600
     note(f"linear split-K garbage workspace M={M} N={N} K={K}")
-    assert split_of(M, N, K) == 4
+    assert split_of(M, N, K) == 3
     W = synth.gaussian((N, K), 9152, 0.02)
     X = synth.gaussian((M, K), 9652)
-    ref = oracle_layer(W, X)
+    g = oracle.absmean(W)
+    T = oracle.ternarize(W, g)
+    Q, s, qs = oracle.quant_act(X)
+    rows = sampled_rows(M)
+    acc_ref = oracle.ternary_matmul(T, Q[rows])
     pw = gpu_pack(W)
     ws = torch.full((bt.linear_workspace_bytes(M, N, K),), 0xFF, dtype=torch.uint8, device=DEV)
     for _ in range(2):
         Y, acc = bt.linear(to_dev(X), pw, want_acc=True, workspace=ws)
-        np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
-        assert tol_ok(Y.cpu().numpy(), ref["Y"])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy()[rows], acc_ref)
+        assert tol_ok(Y.cpu().numpy()[rows], oracle.scale_epilogue(acc_ref, g, s[rows]))
 
 
 @pytest.mark.parametrize("j,name,N,K", [(j, *s) for j, s in enumerate(synth.SHAPES_2B)])

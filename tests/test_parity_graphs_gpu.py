@@ -1,12 +1,12 @@
 """The whole-layer calls under HIP graph capture. Each route of bt_ternary_linear (the fused
-decode kernel at eight and at two k-splits, quantizer + staged GEMV, quantizer + GEMM with
-every tile split in K, quantizer + GEMM with the last round split) and bt_ternary_linear_static
-is captured once and replayed with new inputs. Between replays the program runs its own eager
-work on the same workspace and synchronizes; every replay must give acc and Y bit-identical to
-an eager call on the same inputs (the split-K arrival counters, which the quantizer launch
-zero-fills and the last split resets, must be back at zero for every replay). The eager calls
-themselves are checked against the oracle by the other parity modules; here the small cases
-are also checked against the oracle directly.
+decode kernel at eight and at two k-splits, quantizer + staged GEMV, quantizer + the small-M
+GEMM, quantizer + GEMM with every tile split in K, quantizer + GEMM with the last round split)
+and bt_ternary_linear_static is captured once and replayed with new inputs. Between replays
+the program runs its own eager work on the same workspace and synchronizes; every replay must
+give acc and Y bit-identical to an eager call on the same inputs (the split-K arrival
+counters, which the quantizer launch zero-fills and the last split resets, must be back at
+zero for every replay). The eager calls themselves are checked against the oracle by the
+other parity modules; here the small cases are also checked against the oracle directly.
 """
 import os
 import subprocess
@@ -35,9 +35,11 @@ def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
     return x.shape == y.shape and np.array_equal(x.view(np.uint32), y.view(np.uint32))
 
 
-# (M, N, K): fused S = 8, fused S = 2, quantizer + staged GEMV, quantizer + GEMM split in K
-# (every tile), quantizer + GEMM with the last round's tiles split.
-ROUTES = [(1, 3840, 2560), (4, 13824, 2560), (16, 2560, 2560), (256, 2560, 2560), (2048, 2560, 6912)]
+# (M, N, K): fused S = 8, fused S = 2, quantizer + staged GEMV, quantizer + the small-M GEMM
+# form, quantizer + GEMM split in K (every tile), quantizer + GEMM with the last round's tiles
+# split.
+ROUTES = [(1, 3840, 2560), (4, 13824, 2560), (16, 2560, 2560), (256, 2560, 2560), (300, 3500, 2600),
+          (2048, 2560, 6912)]
 
 
 @pytest.mark.parametrize("static", [False, True], ids=["workspace", "static"])

@@ -75,7 +75,8 @@ def test_pack_rows_empty_k():
 
 
 # (M, N, K, groups) on each route of bt_ternary_linear_rs: fused (M <= 4), quantizer +
-# direct GEMV (M <= 16), quantizer + GEMM (M > 16, split-K where the shape splits).
+# direct GEMV (M <= 16), quantizer + GEMM (M > 16: here the small-M form k_gemm_ks, whose
+# few tiles split their k-steps inside the workgroup).
 LINEAR_CASES = [(1, 768, 300, [640, 64, 64]), (3, 200, 1000, None), (4, 130, 517, [130]),
                 (1, 3840, 2560, [2560, 640, 640]), (2, 9000, 1000, [4500, 4500]),
                 (8, 768, 700, [640, 64, 64]), (16, 600, 2560, None),
@@ -111,7 +112,7 @@ def test_gemv_rows(M, algo):
 
 
 def test_gemm_rows_split_and_plain():
-    M, N, K, groups = 100, 2500, 6900, [2000, 250, 250]
+    M, N, K, groups = 330, 3000, 1700, [2000, 500, 500]
     note(f"gemm_rs M={M} N={N} K={K}")
     W = grouped(N, K, groups, 8700)
     X = synth.gaussian((M, K), 8701)
@@ -119,7 +120,7 @@ def test_gemm_rows_split_and_plain():
     pw = bt.pack_weights_rows(to_dev(W), groups)
     q = bt.quant_act(to_dev(X))
     ws = bt.gemm_workspace(M, N, K, DEV)
-    assert ws is not None  # this shape takes the split-K route
+    assert bt.gemm_split_plan(M, N, K) == (0, 2)  # this shape takes the split-K route
     Y1, acc1 = bt.ternary_gemm(pw, q, want_acc=True)
     Y2, acc2 = bt.ternary_gemm(pw, q, want_acc=True, workspace=ws)
     torch.cuda.synchronize()
