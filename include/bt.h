@@ -198,8 +198,11 @@ bt_status bt_ternary_gemv_rs(const void *Wp, const float *row_scale, const int8_
 /*
  * bt_ternary_gemm -- prefill product for any M >= 1 on int8 MFMA: the packed
  * weight tiles are unpacked in registers straight into MFMA operands, the int8
- * activation tiles are staged in LDS, and the scale epilogue is fused. Same
- * arguments and results as bt_ternary_gemv, with no limit on M. Follows the BitNet
+ * activation tiles are staged in LDS, and the scale epilogue is fused. Shapes with
+ * K >= 512 and at most 256 output tiles of 64 x 64 (e.g. a few hundred tokens) split
+ * each tile's K range over the four waves of its workgroup and sum the parts in LDS;
+ * others take 64 x 256 tiles. Same arguments and results as bt_ternary_gemv, with no
+ * limit on M. Follows the BitNet
  * GPU guide, "Key Components and Source Code Architecture" (prefill is the
  * compute-bound phase) and the "BitCompute" page, "Future Roadmap" (moving the
  * ternary product onto the matrix cores).
@@ -232,7 +235,8 @@ size_t bt_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * workgroups when given its workspace (host-only query, no device call). Output tiles are
  * 64 tokens x 256 weight rows; the first *full_tiles of the library's tile order are
  * computed whole and each later one is split over *splits workgroups (each over a
- * contiguous share of K). *splits == 1: no split (bt_gemm_workspace_bytes is then 0);
+ * contiguous share of K). The shapes that bt_ternary_gemm splits inside its workgroups
+ * (see there) report every tile whole. *splits == 1: no split (bt_gemm_workspace_bytes is then 0);
  * *full_tiles == 0 with *splits > 1: every tile is split. The workspace's leading
  * (tiles - *full_tiles) 32-bit words are the arrival counters of the split tiles.
  *   full_tiles, splits   host pointers, written on BT_OK.
