@@ -522,6 +522,22 @@ __global__ __launch_bounds__(kKsWaves * 64) void k_gemm_ks(
     const int64_t m0 = (int64_t)tm * 64;
     const int64_t n0 = (int64_t)tn * 64;
 
+    // The epilogue's inputs, requested first so that their round trip overlaps the main
+    // loop: the scales of the lane's four weight rows 16 i + r, the statistics of its four
+    // tokens 16 wave + 4 g + v (clamped: rows past N and tokens past M are never stored).
+    float gam_i[4];
+    int32_t xs_v[4];
+    float sx_v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        gam_i[i] = w_scale[rows ? min(n0 + 16 * i + r, N - 1) : 0];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t m = min(m0 + 16 * wave + 4 * g + v, M - 1);
+        xs_v[v] = xsum[m];
+        sx_v[v] = sx[m];
+    }
+
     // This wave's steps: [step0, step0 + nsteps) of the tile's ceil(KC / 2).
     const int nsteps_all = (KC + 1) / 2;
     const int per = (nsteps_all + kKsWaves - 1) / kKsWaves;
@@ -664,18 +680,10 @@ __global__ __launch_bounds__(kKsWaves * 64) void k_gemm_ks(
             d[i] += *reinterpret_cast<const v4i *>(area(wave) + ((s * 4 + i) * 64 + lane) * 16);
 
     // Epilogue of token tile `wave`: lane (g, r) holds tokens 16 wave + 4 g + v, row 16 i + r.
-    int32_t xs_v[4];
-    float sx_v[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int64_t m = min(m0 + 16 * wave + 4 * g + v, M - 1);
-        xs_v[v] = xsum[m];
-        sx_v[v] = sx[m];
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t n = n0 + 16 * i + r;
-        const float gam = w_scale[rows ? min(n, N - 1) : 0];
+        const float gam = gam_i[i];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int64_t m = m0 + 16 * wave + 4 * g + v;
