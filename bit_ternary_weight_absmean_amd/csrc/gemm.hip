@@ -742,8 +742,8 @@ int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + kBM - 1) / kBM) * ((N + 
 //    amortize its prologue, epilogue and the partial-tile hand-off through memory.
 // The small-M form (k_gemm_ks): at least four 128-k steps (one per wave), and few enough
 // 64 x 64 tiles for one workgroup per CU at a time. Measured on the 2B prefill shapes:
-// M = 256 QKV 12.6 -> 10.0 us, O 12.1 -> 9.9, down 16.5 -> 14.9 against the split-K form
-// (step 2.07 -> 1.91 ms); at M = 512 (320-480 tiles, two rounds) it was 5-35% slower.
+// M = 256 QKV 12.6 -> 9.0 us, O 12.1 -> 8.9, down 16.5 -> 13.8 against the split-K form
+// (step 2.07 -> 1.80 ms); at M = 512 (320-480 tiles, two rounds) it was 5-35% slower.
 static bool gemm_small_form(int64_t M, int64_t N, int64_t K)
 {
     const int64_t tiles64 = ((M + 63) / 64) * ((N + 63) / 64);
