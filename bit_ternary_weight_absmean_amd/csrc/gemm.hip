@@ -482,12 +482,13 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
 // For products whose 64 x 256 tiles would leave most CUs idle (a few hundred tokens against
 // a few thousand rows): 64 x 64 output tiles, one per workgroup of four waves, with the
 // tile's 128-k steps split four ways inside the workgroup. Wave w streams a contiguous
-// share of the steps through NS stages of its own (each stage: the step's 64 x 128
-// activation block and 64 x 32 packed weight block, brought by direct loads in k_gemm's
-// LDS layouts), so the main loop has no workgroup barrier: a wave's own waits order its
-// loads and its reads. The four partial tiles then meet in LDS, and wave w finishes token
-// rows 16 w .. 16 w + 15 of the tile. Against k_gemm's split-K form the partial tiles
-// never leave the CU, and every tile gets a whole CU's four SIMDs.
+// share of the steps through NS stages of its own (NS = 3 at one workgroup per CU, 2 where
+// two share a CU; each stage: the step's 64 x 128 activation block and 64 x 32 packed
+// weight block, brought by direct loads in k_gemm's LDS layouts), so the main loop has no
+// workgroup barrier: a wave's own waits order its loads and its reads. The four partial
+// tiles then meet in LDS, and wave w finishes token rows 16 w .. 16 w + 15 of the tile.
+// Against k_gemm's split-K form the partial tiles never leave the CU (no workspace), and
+// the work spreads over more CUs in shorter shares.
 constexpr int kKsWaves = 4;
 constexpr int kKsA = 64 * kBK;         // activation block of a step: 64 rows x 128 bytes
 constexpr int kKsB = 64 * kBK / 4;     // packed weight block of a step: 64 rows x 32 bytes
@@ -500,12 +501,12 @@ __global__ __launch_bounds__(kKsWaves * 64) void k_gemm_ks(
     const float *__restrict__ sx, const int32_t *__restrict__ xsum, int64_t M, int64_t N, int KC, int tiles_m,
     int tiles, int per_xcd, float *__restrict__ Y, int32_t *__restrict__ ACC, int rows)
 {
-    static_assert(NS == 3, "three stages (the ring below is written for three)");
+    static_assert(NS == 2 || NS == 3, "a ring of two or three stages");
     // One array per ring stage, each holding the four waves' copies of that stage (as in
     // k_gemm: distinct objects let the compiler tell which stage a direct load writes).
     __shared__ __attribute__((aligned(1024))) int8_t lds0[kKsWaves * kKsStage];
     __shared__ __attribute__((aligned(1024))) int8_t lds1[kKsWaves * kKsStage];
-    __shared__ __attribute__((aligned(1024))) int8_t lds2[kKsWaves * kKsStage];
+    __shared__ __attribute__((aligned(1024))) int8_t lds2[NS > 2 ? kKsWaves * kKsStage : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -631,21 +632,31 @@ __global__ __launch_bounds__(kKsWaves * 64) void k_gemm_ks(
     if (nsteps > 0) {
         issue(0, lds0);
         issue(min(1, last), lds1);
-        issue(min(2, last), lds2);
+        if constexpr (NS > 2)
+            issue(min(2, last), lds2);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * kKsLoads));
         asm volatile("" ::: "memory");
         read_a(lds0, a_off0, fa0);
         read_b(lds0, fb);
         int st = 0;
-        for (; st + NS <= nsteps; st += NS) {
-            step(lds0, lds1, st);
-            step(lds1, lds2, st + 1);
-            step(lds2, lds0, st + 2);
+        if constexpr (NS == 3) {
+            for (; st + NS <= nsteps; st += NS) {
+                step(lds0, lds1, st);
+                step(lds1, lds2, st + 1);
+                step(lds2, lds0, st + 2);
+            }
+            if (st < nsteps)
+                step(lds0, lds1, st);
+            if (st + 1 < nsteps)
+                step(lds1, lds2, st + 1);
+        } else {
+            for (; st + NS <= nsteps; st += NS) {
+                step(lds0, lds1, st);
+                step(lds1, lds0, st + 1);
+            }
+            if (st < nsteps)
+                step(lds0, lds1, st);
         }
-        if (st < nsteps)
-            step(lds0, lds1, st);
-        if (st + 1 < nsteps)
-            step(lds1, lds2, st + 1);
     }
     // The trailing (clamped, unused) loads retire, then every wave is done with the rings.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -740,14 +751,19 @@ int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + kBM - 1) / kBM) * ((N + 
 //  * Otherwise every tile split in 2-4 (full = 0): it pays when the tiles alone leave most
 //    of the 768 workgroup slots (three per CU) empty and every split keeps enough steps to
 //    amortize its prologue, epilogue and the partial-tile hand-off through memory.
-// The small-M form (k_gemm_ks): at least four 128-k steps (one per wave), and few enough
-// 64 x 64 tiles for one workgroup per CU at a time. Measured on the 2B prefill shapes:
-// M = 256 QKV 12.6 -> 9.0 us, O 12.1 -> 8.9, down 16.5 -> 13.8 against the split-K form
-// (step 2.07 -> 1.80 ms); at M = 512 (320-480 tiles, two rounds) it was 5-35% slower.
+// The small-M form (k_gemm_ks): at least four 128-k steps (one per wave), and at most two
+// 64 x 64 tiles per CU: up to 256 tiles one workgroup per CU with a 3-stage ring (120 KB of
+// LDS), up to 512 two per CU with a 2-stage ring (80 KB). Measured on the 2B prefill shapes
+// against k_gemm (split-K where it splits), us per launch in the step:
+//  * M = 256: QKV 12.6 -> 9.0, O 12.1 -> 8.9, down 16.5 -> 13.8 (step 2.07 -> 1.80 ms);
+//  * M = 512: QKV 17.3 -> 11.7, O 12.6 -> 11.6, down 22.4 -> 20.2 (step 2.75 -> 2.48 ms),
+//    where a 3-stage ring at one workgroup per CU (two rounds) was 5-35% slower;
+//  * M = 768: O and down (480 tiles) 17.1 -> 11.5 and 24.4 -> 20.7, but QKV (720 tiles)
+//    14.4 -> 18.3, and at M = 1024 (640-960 tiles) QKV 15.0 -> 22.0, O 14.7 -> 18.2.
 static bool gemm_small_form(int64_t M, int64_t N, int64_t K)
 {
     const int64_t tiles64 = ((M + 63) / 64) * ((N + 63) / 64);
-    return M > 0 && N > 0 && K >= 4 * 128 && tiles64 <= kCUs;
+    return M > 0 && N > 0 && K >= 4 * 128 && tiles64 <= 2 * kCUs;
 }
 
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K)
@@ -789,9 +805,14 @@ hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, bool row_scales, c
     if (gemm_small_form(M, N, K)) {
         const int64_t tiles_m = (M + 63) / 64, tiles64 = tiles_m * ((N + 63) / 64);
         const int per_xcd = (int)((tiles64 + kXcds - 1) / kXcds);
-        hipLaunchKernelGGL((k_gemm_ks<3>), dim3((unsigned)(per_xcd * kXcds)), dim3(kKsWaves * 64), 0, s, Wp, w_scale,
-                           Xq, ldq, sx, xsum, M, N, (int)((K + 63) / 64), (int)tiles_m, (int)tiles64, per_xcd, Y, acc,
-                           row_scales ? 1 : 0);
+        const dim3 grid((unsigned)(per_xcd * kXcds)), block(kKsWaves * 64);
+        const int KC = (int)((K + 63) / 64), rows = row_scales ? 1 : 0;
+        if (tiles64 <= kCUs)
+            hipLaunchKernelGGL((k_gemm_ks<3>), grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, M, N, KC,
+                               (int)tiles_m, (int)tiles64, per_xcd, Y, acc, rows);
+        else
+            hipLaunchKernelGGL((k_gemm_ks<2>), grid, block, 0, s, Wp, w_scale, Xq, ldq, sx, xsum, M, N, KC,
+                               (int)tiles_m, (int)tiles64, per_xcd, Y, acc, rows);
         return hipGetLastError();
     }
     // Otherwise 64 x 256 blocks of 4 waves, three workgroups per CU (3-stage ring, 48 KB of
@@ -814,7 +835,8 @@ hipError_t launch_gemm(const uint4 *Wp, const float *w_scale, bool row_scales, c
 int plan_gemm(int64_t M, int64_t N, int64_t K, bool row_scales, bool split_workspace, char *buf, size_t len)
 {
     if (gemm_small_form(M, N, K))
-        return snprintf(buf, len, "k_gemm_ks<NS=3,ROWS=%d>", (int)row_scales);
+        return snprintf(buf, len, "k_gemm_ks<NS=%d,ROWS=%d>", ((M + 63) / 64) * ((N + 63) / 64) <= kCUs ? 3 : 2,
+                        (int)row_scales);
     const GemmPlan pl = gemm_plan(M, N, K);
     const int64_t tiles = gemm_tiles(M, N);
     if (!split_workspace || pl.nsplit == 1)

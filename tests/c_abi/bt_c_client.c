@@ -287,8 +287,9 @@ int main(void)
         {4, 2560, 6912},   /* 2B-class down at four tokens (fused route) */
         {16, 2560, 2560},  /* sixteen tokens (quantizer + staged GEMV) */
         {5, 200, 301},     /* ragged rows and columns, K % 4 != 0 */
-        {256, 2560, 2560}, /* prefill, few tiles (the small-M form) */
-        {300, 3500, 2600}, /* prefill with K split over workgroups */
+        {256, 2560, 2560}, /* prefill, few tiles (the small-M form, one workgroup per CU) */
+        {300, 3500, 2600}, /* prefill, the small-M form at two workgroups per CU */
+        {700, 3000, 4000}, /* prefill with K split over workgroups */
     };
     for (size_t c = 0; c < sizeof cases / sizeof cases[0]; ++c)
         run_case(s, cases[c][0], cases[c][1], cases[c][2], 1000 + c);

@@ -76,12 +76,13 @@ def test_gemm_split_plan():
         (2048, 2560, 6912): (256, 4),
         (4096, 2560, 6912): (512, 2),   # 640 tiles: the last 128 in two
         (1024, 13824, 2560): (864, 1),  # tail of 96 tiles, but shares of 10 steps: whole
-        # few 64 x 64 tiles (at most one per CU) and K >= 512: the small-M form, no split
+        # at most two 64 x 64 tiles per CU (512) and K >= 512: the small-M form, no split
         (256, 3840, 2560): (60, 1), (256, 2560, 6912): (40, 1), (100, 2500, 6900): (20, 1),
         (70, 600, 2500): (6, 1), (65, 300, 1600): (4, 1), (256, 4096, 512): (64, 1),
+        (520, 2500, 6900): (90, 1), (300, 3500, 2600): (70, 1), (512, 3840, 2560): (120, 1),
         # more 64 x 64 tiles, few 64 x 256 ones: every tile split
-        (520, 2500, 6900): (0, 4), (300, 3500, 2600): (0, 3), (280, 4500, 1700): (0, 2),
-        (256, 13824, 2560): (216, 1), (70, 600, 500): (6, 1),
+        (600, 3500, 6900): (0, 4), (650, 3300, 5500): (0, 3), (700, 3000, 4000): (0, 2),
+        (1024, 2560, 6912): (0, 4), (256, 13824, 2560): (216, 1), (70, 600, 500): (6, 1),
         (1100, 4096, 6200): (256, 4), (250, 22700, 3100): (256, 2),
         (5, 5, 0): (1, 1), (0, 5, 5): (0, 1),
     }
@@ -90,8 +91,9 @@ def test_gemm_split_plan():
         assert bt.lib().bt_gemm_workspace_bytes(M, N, K) == ws_bytes(M, N, *want), (M, N, K)
     # which kernel each form runs
     for (M, N, K), kern in {(256, 3840, 2560): "k_gemm_ks<NS=3,ROWS=0>", (256, 4096, 512): "k_gemm_ks<NS=3,ROWS=0>",
-                            (256, 4160, 512): "k_gemm<SPLITK=0", (256, 3840, 511): "k_gemm<SPLITK=0",
-                            (300, 3500, 2600): "k_gemm<SPLITK=1"}.items():
+                            (256, 4160, 512): "k_gemm_ks<NS=2,ROWS=0>", (512, 4096, 512): "k_gemm_ks<NS=2,ROWS=0>",
+                            (520, 4160, 512): "k_gemm<SPLITK=0", (256, 3840, 511): "k_gemm<SPLITK=0",
+                            (650, 3300, 5500): "k_gemm<SPLITK=1"}.items():
         assert bt.kernel_plan(bt.CALL_GEMM_WS, M, N, K).startswith(kern), (M, N, K)
     full, splits = ctypes.c_int64(), ctypes.c_int32()
     assert bt.lib().bt_gemm_split_plan(-1, 5, 5, ctypes.byref(full), ctypes.byref(splits)) == BT_ERR_SHAPE

@@ -162,10 +162,11 @@ def test_gemv_small(M, N, K, algo):
 # (1024, 8448, 512): 528 tiles, more than one round of workgroups. K >= 512 with at most
 # 256 tiles of 64 x 64 takes the small-M form (k_gemm_ks): (300, 200, 517), (64, 1000, 2560),
 # (257, 516, 700), and its k-share edges: 4 steps (one per wave), 5 steps of 9 chunks
-# (shares 2, 2, 1, 0), 5 whole steps, and exactly 256 tiles.
+# (shares 2, 2, 1, 0), 5 whole steps, exactly 256 tiles (3-stage ring, one workgroup per CU)
+# and 257 to 512 tiles (2-stage ring, two per CU; ragged, and exactly 512).
 GEMM_SMALL = [(1, 64, 64), (17, 100, 300), (128, 512, 256), (129, 130, 129), (300, 200, 517), (64, 1000, 2560),
               (257, 516, 700), (1024, 8448, 512), (64, 64, 512), (200, 700, 513), (100, 130, 640),
-              (256, 4096, 1024)]
+              (256, 4096, 1024), (300, 3500, 900), (512, 4096, 768)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SMALL)
@@ -259,9 +260,9 @@ def test_100b_down_decode_m16():
 
 
 # Split-K route (bt_ternary_gemm_ws): shapes chosen so that the split heuristic picks
-# 4, 3 and 2 workgroups for every tile, ragged in M, N and K (more 64 x 64 tiles than CUs,
-# so the small-M form does not take them).
-SPLIT_SHAPES = [(520, 2500, 6900, 4), (300, 3500, 2600, 3), (280, 4500, 1700, 2)]
+# 4, 3 and 2 workgroups for every tile, ragged in M, N and K (more than 512 tiles of
+# 64 x 64, so the small-M form does not take them).
+SPLIT_SHAPES = [(600, 3500, 6900, 4), (650, 3300, 5500, 3), (700, 3000, 4000, 2)]
 
 
 def split_of(M, N, K):
@@ -341,7 +342,7 @@ def test_gemm_tail_split(M, N, K, full, S):
 
 
 def test_gemm_split_k_small_workspace_falls_back():
-    M, N, K = 300, 3500, 2600
+    M, N, K = 700, 3000, 4000
     note(f"gemm split-K short workspace M={M} N={N} K={K}")
     W = synth.gaussian((N, K), 9151, 0.02)
     X = synth.gaussian((M, K), 9651)
@@ -579,7 +580,7 @@ def test_linear_tail_split_garbage_workspace():
 def test_linear_split_k_garbage_workspace():
     """bt_ternary_linear on a shape whose GEMM splits K, with a workspace full of garbage:
     the call initializes everything it reads (the quantizer zero-fills the counters)."""
-    M, N, K = 300, 3500, 2600
+    M, N, K = 650, 3300, 5500
     note(f"linear split-K garbage workspace M={M} N={N} K={K}")
     assert split_of(M, N, K) == 3
     W = synth.gaussian((N, K), 9152, 0.02)

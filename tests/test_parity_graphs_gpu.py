@@ -36,10 +36,10 @@ def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
 
 
 # (M, N, K): fused S = 8, fused S = 2, quantizer + staged GEMV, quantizer + the small-M GEMM
-# form, quantizer + GEMM split in K (every tile), quantizer + GEMM with the last round's tiles
-# split.
+# form (3-stage and 2-stage ring), quantizer + GEMM split in K (every tile), quantizer + GEMM
+# with the last round's tiles split.
 ROUTES = [(1, 3840, 2560), (4, 13824, 2560), (16, 2560, 2560), (256, 2560, 2560), (300, 3500, 2600),
-          (2048, 2560, 6912)]
+          (650, 3300, 5500), (2048, 2560, 6912)]
 
 
 @pytest.mark.parametrize("static", [False, True], ids=["workspace", "static"])

@@ -112,11 +112,12 @@ def test_gemv_rows(M, algo):
 
 
 def test_gemm_rows_split_and_plain():
-    M, N, K, groups = 330, 3000, 1700, [2000, 500, 500]
+    M, N, K, groups = 700, 3000, 4000, [2000, 500, 500]
     note(f"gemm_rs M={M} N={N} K={K}")
     W = grouped(N, K, groups, 8700)
     X = synth.gaussian((M, K), 8701)
-    ref = oracle.linear_rows(W, X, groups)
+    rows = np.concatenate([np.arange(3, M, 29), [M - 1]])  # token rows in every 64-token tile row
+    ref = oracle.linear_rows(W, X[rows], groups)
     pw = bt.pack_weights_rows(to_dev(W), groups)
     q = bt.quant_act(to_dev(X))
     ws = bt.gemm_workspace(M, N, K, DEV)
@@ -124,10 +125,10 @@ def test_gemm_rows_split_and_plain():
     Y1, acc1 = bt.ternary_gemm(pw, q, want_acc=True)
     Y2, acc2 = bt.ternary_gemm(pw, q, want_acc=True, workspace=ws)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(acc1.cpu().numpy(), ref["acc"])
-    np.testing.assert_array_equal(acc2.cpu().numpy(), ref["acc"])
+    np.testing.assert_array_equal(acc1.cpu().numpy()[rows], ref["acc"])
+    np.testing.assert_array_equal(acc2.cpu().numpy(), acc1.cpu().numpy())
     np.testing.assert_array_equal(Y1.cpu().numpy(), Y2.cpu().numpy())
-    assert tol_ok(Y1.cpu().numpy(), ref["Y"])
+    assert tol_ok(Y1.cpu().numpy()[rows], ref["Y"])
 
 
 def test_gemm_rows_tail_split():
