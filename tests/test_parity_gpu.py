@@ -163,10 +163,11 @@ def test_gemv_small(M, N, K, algo):
 # 256 tiles of 64 x 64 takes the small-M form (k_gemm_ks): (300, 200, 517), (64, 1000, 2560),
 # (257, 516, 700), and its k-share edges: 4 steps (one per wave), 5 steps of 9 chunks
 # (shares 2, 2, 1, 0), 5 whole steps, exactly 256 tiles (3-stage ring, one workgroup per CU)
-# and 257 to 512 tiles (2-stage ring, two per CU; ragged, and exactly 512).
+# and 257 to 512 tiles (2-stage ring, two per CU; ragged, and exactly 512); and the longest
+# rows (K = 28672: 112 steps, 28 per wave).
 GEMM_SMALL = [(1, 64, 64), (17, 100, 300), (128, 512, 256), (129, 130, 129), (300, 200, 517), (64, 1000, 2560),
               (257, 516, 700), (1024, 8448, 512), (64, 64, 512), (200, 700, 513), (100, 130, 640),
-              (256, 4096, 1024), (300, 3500, 900), (512, 4096, 768)]
+              (256, 4096, 1024), (300, 3500, 900), (512, 4096, 768), (40, 1000, 28672)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SMALL)

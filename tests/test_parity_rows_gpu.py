@@ -80,7 +80,8 @@ def test_pack_rows_empty_k():
 LINEAR_CASES = [(1, 768, 300, [640, 64, 64]), (3, 200, 1000, None), (4, 130, 517, [130]),
                 (1, 3840, 2560, [2560, 640, 640]), (2, 9000, 1000, [4500, 4500]),
                 (8, 768, 700, [640, 64, 64]), (16, 600, 2560, None),
-                (40, 768, 700, [640, 64, 64]), (100, 2500, 6900, [1000, 1500]), (300, 257, 1000, None)]
+                (40, 768, 700, [640, 64, 64]), (100, 2500, 6900, [1000, 1500]), (300, 257, 1000, None),
+                (520, 2100, 700, [1000, 1100])]
 
 
 @pytest.mark.parametrize("M,N,K,groups", LINEAR_CASES)
