@@ -923,11 +923,14 @@ def summarize_trace(args):
         lines.append(f"| `{name}` | {grid} | {wg} | {len(d)} | {statistics.mean(d):.3f} | {statistics.median(d):.3f} "
                      f"| {len(gp)} | {statistics.mean(gp) if gp else float('nan'):.3f} | "
                      f"{statistics.median(gp) if gp else float('nan'):.3f} |")
+    def is_kernel(name, kname):  # k_gemm, not k_gemm_ks; k_gemv_direct and k_gemv_direct_db
+        return re.search(rf"\b{kname}(_db)?[<(]", name) is not None
+
     # every product kernel of the workload together
     for kname in ("k_linear_decode", "k_gemv_staged", "k_gemv_blocked", "k_gemv_direct", "k_gemv_lut", "k_gemv_bits",
-                  "k_gemm"):
-        d = [x for (n, _, _), e in per.items() if kname in n for x in e["dur"]]
-        gp = [x for (n, _, _), e in per.items() if kname in n for x in e["gap"]]
+                  "k_gemm", "k_gemm_ks"):
+        d = [x for (n, _, _), e in per.items() if is_kernel(n, kname) for x in e["dur"]]
+        gp = [x for (n, _, _), e in per.items() if is_kernel(n, kname) for x in e["gap"]]
         if d:
             lines += ["", f"All `{kname}` dispatches: {len(d)}, mean duration {statistics.mean(d):.3f} us, "
                           f"mean interval {statistics.mean(gp) if gp else float('nan'):.3f} us over {len(gp)} "
@@ -945,9 +948,15 @@ def summarize_trace(args):
     # the workload's dominant kernel, for the benchmark line (read back while the sources match)
     spec = workload_spec(args.workload, args.m)
     kname = dominant_kernel_name(spec, args)
-    d = [x for (n, _, _), e in per.items() if kname in n for x in e["dur"]]
-    gp = [x for (n, _, _), e in per.items() if kname in n for x in e["gap"]]
-    if d:
+    d = [x for (n, _, _), e in per.items() if is_kernel(n, kname) for x in e["dur"]]
+    gp = [x for (n, _, _), e in per.items() if is_kernel(n, kname) for x in e["gap"]]
+    # one figure per launch only where every matrix of the step runs that kernel
+    single = all(re.search(rf"\b{kname}<", p) for p in step_plans(spec, getattr(args, "split", False)))
+    if d and not single:
+        kernels = dict.fromkeys(k for p in step_plans(spec) for k in re.findall(r"k_\w+", p) if "quant" not in k)
+        lines += ["", f"The step runs more than one product kernel ({', '.join(kernels)}): no single",
+                  "per-launch figure is recorded for it."]
+    if d and single:
         M = spec["M"]
         alg = [linear_bytes(M, N, K) if kname == "k_linear_decode" else gemv_bytes(M, N, K)
                for _, N, K in spec["shapes"]]
