@@ -25,7 +25,7 @@ namespace {
 
 constexpr int kLutWaves = 4;
 constexpr int kLutRows = 16;   // weight rows per workgroup: lane = 4 * row + word
-constexpr int kLutUnroll = 4;  // chunks in flight per wave
+constexpr int kLutBatch = 8;   // chunks per weight batch (two batches in flight per wave)
 constexpr int kLutBuild = 8;   // tables whose activation bytes each thread loads together
 
 template <int CTRL>
@@ -48,15 +48,33 @@ __global__ __launch_bounds__(kLutWaves * 64) void k_gemv_lut(const uint32_t *__r
     const int wave = uniform(tid >> 6);
     const int KG = KC * 4;
 
+    // Lane (r, j) = (lane / 4, lane % 4) reads word j of row r's 16 bytes in each chunk the
+    // wave owns (chunks wave, wave + 4, ...): 256 contiguous bytes per wave and chunk. Rows
+    // past N (up to the packed 64-row padding) are read and never stored.
+    const int r = lane >> 2, j = lane & 3;
+    const int64_t n = (int64_t)blockIdx.x * kLutRows + r;
+    const int64_t rb = n >> 6, rr = n & 63;
+    const uint32_t *wrow = Wp + (rb * KC * 64 + rr) * 4 + j;  // + 256 words per chunk
+    const int nmine = wave < KC ? (KC - 1 - wave) / kLutWaves + 1 : 0;
+    const int nb = (nmine + kLutBatch - 1) / kLutBatch;
+    uint32_t wa[kLutBatch], wb[kLutBatch];
+    auto load_batch = [&](uint32_t (&w)[kLutBatch], int b) {  // unconditional, at clamped chunks
+#pragma unroll
+        for (int u = 0; u < kLutBatch; ++u)
+            w[u] = wrow[(int64_t)min(wave + kLutWaves * (b * kLutBatch + u), KC - 1) * 256];
+    };
+
     // 1. The tables: thread t fills the tables (g, p) = t, t + 256, ... (16 entries,
     //    two 16-byte LDS stores each). Xq rows are zero past K up to a multiple of 256,
     //    so every k read here lies in the row. The two activation bytes of kLutBuild
     //    tables are loaded together (unconditionally, at clamped tables) before any is
-    //    built: loaded one table at a time, every table waited a round trip of its own.
+    //    built. The first such loads go out before the wave's first two weight batches
+    //    (vector-memory loads complete in order: building then waits for the activation
+    //    bytes only, while the weights stream in under it).
     constexpr int T = kLutWaves * 64;
     const int npairs = KG * 8;
-    for (int base = tid; base < npairs; base += T * kLutBuild) {
-        int q0[kLutBuild], q1[kLutBuild];
+    int q0[kLutBuild], q1[kLutBuild];
+    auto load_q = [&](int base) {
 #pragma unroll
         for (int i = 0; i < kLutBuild; ++i) {
             const int pair = min(base + i * T, npairs - 1);
@@ -65,6 +83,13 @@ __global__ __launch_bounds__(kLutWaves * 64) void k_gemv_lut(const uint32_t *__r
             q0[i] = Xq[k0];
             q1[i] = Xq[k0 + 4];
         }
+    };
+    load_q(tid);
+    load_batch(wa, 0);
+    load_batch(wb, 1);
+    for (int base = tid; base < npairs; base += T * kLutBuild) {
+        if (base != tid)
+            load_q(base);
 #pragma unroll
         for (int i = 0; i < kLutBuild; ++i) {
             const int pair = base + i * T;
@@ -85,34 +110,31 @@ __global__ __launch_bounds__(kLutWaves * 64) void k_gemv_lut(const uint32_t *__r
     }
     __syncthreads();
 
-    // 2. Lookups. Lane (r, j) = (lane / 4, lane % 4) reads word j of row r's 16 bytes in
-    //    each chunk the wave owns (chunks wave, wave + 4, ...): 256 contiguous bytes per
-    //    wave and chunk. Rows past N (up to the packed 64-row padding) are read and never
-    //    stored.
-    const int r = lane >> 2, j = lane & 3;
-    const int64_t n = (int64_t)blockIdx.x * kLutRows + r;
-    const int64_t rb = n >> 6, rr = n & 63;
-    const uint32_t *wrow = Wp + (rb * KC * 64 + rr) * 4 + j;  // + 256 words per chunk
+    // 2. Lookups, one batch while the next one's loads are in flight: pairs of batches
+    //    with unconditional loads, then the last pair with none.
     const int16_t *tab = reinterpret_cast<const int16_t *>(smem);
     int acc = 0;
-    for (int c0 = wave; c0 < KC; c0 += kLutWaves * kLutUnroll) {
-        uint32_t w[kLutUnroll];
+    auto lookup_batch = [&](const uint32_t (&w)[kLutBatch], int b) {
 #pragma unroll
-        for (int u = 0; u < kLutUnroll; ++u) {
-            const int c = min(c0 + u * kLutWaves, KC - 1);
-            w[u] = wrow[(int64_t)c * 256];
-        }
-#pragma unroll
-        for (int u = 0; u < kLutUnroll; ++u) {
-            const int c = c0 + u * kLutWaves;
-            if (c < KC) {  // wave-uniform
-                const int16_t *t = tab + (4 * c + j) * 128;
+        for (int u = 0; u < kLutBatch; ++u) {
+            const int i = b * kLutBatch + u;
+            if (i < nmine) {  // wave-uniform
+                const int16_t *t = tab + (4 * (wave + kLutWaves * i) + j) * 128;
 #pragma unroll
                 for (int p = 0; p < 8; ++p)
                     acc += t[p * 16 + ((w[u] >> (4 * p)) & 15u)];
             }
         }
+    };
+    int b = 0;
+    for (; b + 2 < nb; b += 2) {
+        lookup_batch(wa, b);
+        load_batch(wa, b + 2);
+        lookup_batch(wb, b + 1);
+        load_batch(wb, b + 3);
     }
+    lookup_batch(wa, b);
+    lookup_batch(wb, b + 1);
 
     // 3. Row sums: the four words of a row (a quad of lanes), then the waves.
     acc += lut_dpp<0xB1>(acc);  // quad_perm [1,0,3,2]
