@@ -71,16 +71,16 @@ def test_pack_binary(N, K):
     torch.cuda.synchronize()
     assert pw.scale.cpu().numpy().view(np.uint32)[0] == oracle.absmax_rows(W.reshape(1, -1)).view(np.uint32)[0]
     words = pw.data.cpu().numpy().view(np.uint32)
-    KC = (K + 127) // 128
-    # word (rb, c, r, j) at index ((rb * KC + c) * 64 + r) * 4 + j holds k = 128 c + 32 j + b
-    Wb = oracle.binarize(W)
-    for n in sorted({0, N // 2, N - 1}):
-        rb, r = divmod(n, 64)
-        for k in range(K):
-            c, rem = divmod(k, 128)
-            j, b = divmod(rem, 32)
-            bit = (int(words[((rb * KC + c) * 64 + r) * 4 + j]) >> b) & 1
-            assert bit == int(Wb[n, k] < 0), (n, k)
+    KC, NB = (K + 127) // 128, (N + 63) // 64
+    # word (rb, c, r, j) at index ((rb * KC + c) * 64 + r) * 4 + j holds k = 128 c + 32 j + b at
+    # bit b of row n = 64 rb + r; every bit of the padded [64 NB, 128 KC] matrix is checked,
+    # the padding (rows past N, k past K) clear.
+    w4 = words[: NB * KC * 64 * 4].reshape(NB, KC, 64, 4)
+    bits = (w4[..., None] >> np.arange(32, dtype=np.uint32)) & 1  # [rb, c, r, j, b]
+    got = bits.transpose(0, 2, 1, 3, 4).reshape(NB * 64, KC * 128).astype(np.uint8)
+    want = np.zeros_like(got)
+    want[:N, :K] = oracle.binarize(W) < 0
+    np.testing.assert_array_equal(got, want)
 
 
 BITS_CASES = [(1, 1, 1), (1, 100, 300), (3, 65, 129), (4, 200, 700), (16, 130, 517), (1, 4096, 4096),
