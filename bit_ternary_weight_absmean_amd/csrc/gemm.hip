@@ -431,21 +431,33 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
         xs_r[c] = s_xsum[row];
         sx_r[c] = s_sx[row];
     }
-#pragma unroll
-    for (int a = 0; a < TM; ++a) {
+    // LDS runs one wave's accesses in issue order, so the slab of token tile a + 1 is written
+    // right behind the reads of tile a (which still see tile a), and those reads are all
+    // issued before any is waited for: one LDS round trip per tile, not one per row.
+    auto write_slab = [&](int a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
 #pragma unroll
             for (int i = 0; i < TN; ++i)
                 slab[(4 * g + v) * kPitchW + 16 * i + r] = acc[a][i][v];
+    };
+    write_slab(0);
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
         const int64_t mt = m0 + wm * 64 + a * 16;  // first token of this 16-row slab
         if (vec) {
+            v4i rows4[4];  // slab rows 4 q + g, columns 4 r .. 4 r + 3
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                rows4[q] = *reinterpret_cast<const v4i *>(slab + (4 * q + g) * kPitchW + 4 * r);
+            if (a + 1 < TM)
+                write_slab(a + 1);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int rr = 4 * q + g;  // slab row of this lane
                 const int64_t m = mt + rr;
                 const int64_t n = n0 + 4 * r;
-                const v4i a4 = *reinterpret_cast<const v4i *>(slab + rr * kPitchW + 4 * r);
+                const v4i a4 = rows4[q];
                 if (m < M && n < N) {
                     const int32_t xs_m = xs_r[4 * a + q];
                     const float sxm = sx_r[4 * a + q];
@@ -474,6 +486,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WP
                         __builtin_nontemporal_store((float)d * (gam.x * sx[m]), Y + m * N + n);
                 }
             }
+            if (a + 1 < TM)
+                write_slab(a + 1);
         }
     }
 }
