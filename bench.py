@@ -102,6 +102,9 @@ def parse():
     p.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "OUT_JSON"),
                    help="write an MFMA-utilization summary for the prefill GEMM from a rocprofv3 --pmc "
                         "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_I8 run of this workload")
+    p.add_argument("--summarize-sq", nargs=3, metavar=("PASS1_DIR", "PASS2_DIR", "OUT_MD"),
+                   help="write the prefill GEMM's per-shape wave-time breakdown from the two rocprofv3 --pmc "
+                        "passes of SQ counters listed in SQ_PASSES, run on this workload")
     p.add_argument("--command", default="", help="the rocprofv3 command line recorded with --summarize-pmc / -mfma")
     return p.parse_args()
 
@@ -877,6 +880,64 @@ def summarize_mfma(args):
     print(json.dumps(out))
 
 
+# The two counter passes of --summarize-sq (eight SQ counters each: one pass holds at most eight).
+SQ_PASSES = (["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+              "SQ_ACTIVE_INST_ANY", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT"],
+             ["SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_MISC",
+              "SQ_INSTS_LDS", "SQ_LDS_ADDR_CONFLICT", "SQ_INST_LEVEL_LDS", "SQ_WAVES"])
+
+
+def summarize_sq(args):
+    """Per-shape wave-time breakdown of k_gemm on the prefill workload from two rocprofv3 --pmc passes
+    (SQ_PASSES), summed over every dispatch of each shape: issuing, VALU share of issue, waiting at
+    s_waitcnt, dependency stalls, LDS bank conflicts per LDS instruction. A dispatch's shape is told
+    by its grid, sized as the GEMM launcher sizes it (the step's route: workspace and split plan)."""
+    d1, d2, out_md = args.summarize_sq
+    spec = workload_spec(args.workload, args.m)
+    if not spec["prefill"]:
+        raise SystemExit("--summarize-sq is for the prefill workload")
+    import bit_ternary_weight_absmean_amd as bt
+
+    M = spec["M"]
+    label = {}
+    for name, N, K in spec["shapes"]:
+        tiles = -(-M // 64) * -(-N // 256)
+        full, splits = bt.gemm_split_plan(M, N, K)
+        full = tiles if splits == 1 else full
+        wgs = 8 * (-(-full // 8) + -(-(tiles - full) // 8) * splits)
+        split = "" if splits == 1 else (f", {full} whole + {tiles - full} split in {splits}" if full
+                                        else f", every tile split in {splits}")
+        label[wgs * 256] = f"{name} {N}x{K} ({tiles} tiles{split})"
+    sums = collections.defaultdict(lambda: collections.defaultdict(float))
+    for d, counters in zip((d1, d2), SQ_PASSES):
+        for c in counters:
+            for r in _pmc_rows(d, c):
+                if "k_gemm<" in r["Kernel_Name"]:
+                    sums[int(r["Grid_Size"])][c] += float(r["Counter_Value"])
+    cmd = ("rocprofv3 --pmc {} --output-format csv -d gpurun_out/{} -o run -- python3 bench.py --workload "
+           f"2b_prefill --m {M} --eager --steps 1 --warmup 1 --no-cpu-baseline --no-ceilings")
+    lines = [f"# k_gemm wave-time breakdown on the 2B prefill workload (M={M}), per shape", "",
+             "Commands (run from the repository root, one pass per counter set), then "
+             f"`python3 bench.py --workload 2b_prefill --m {M} --summarize-sq gpurun_out/sq1 gpurun_out/sq2 <this file>`:",
+             "", "    " + cmd.format(" ".join(SQ_PASSES[0]), "sq1"), "    " + cmd.format(" ".join(SQ_PASSES[1]), "sq2"),
+             "", f"k_gemm source sha256 (comments and blank lines out): `{source_hash('k_gemm')}`.", "",
+             "Sums over every dispatch of each shape in the run. Per-wave cycles are SQ_WAVE_CYCLES / SQ_WAVES (the "
+             "counter's own units); the shares are of SQ_WAVE_CYCLES.", "",
+             "| shape | waves | wave-cycles per wave | issuing (ACTIVE_INST_ANY) | of which VALU | at s_waitcnt "
+             "(WAIT_ANY) | dependency / issue stalls (WAIT_INST_ANY) | LDS bank conflicts per LDS instruction |",
+             "|---|---|---|---|---|---|---|---|"]
+    for grid, c in sorted(sums.items(), key=lambda kv: kv[1]["SQ_WAVES"]):
+        wc = c["SQ_WAVE_CYCLES"] or 1.0
+        lines.append("| {} | {:.0f} | {:.0f} | {:.0%} | {:.0%} | {:.0%} | {:.0%} | {:.2f} |".format(
+            label.get(grid, f"grid {grid}"), c["SQ_WAVES"], wc / max(c["SQ_WAVES"], 1.0),
+            c["SQ_ACTIVE_INST_ANY"] / wc, c["SQ_ACTIVE_INST_VALU"] / max(c["SQ_ACTIVE_INST_ANY"], 1.0),
+            c["SQ_WAIT_ANY"] / wc, c["SQ_WAIT_INST_ANY"] / wc,
+            c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_INSTS_LDS"], 1.0)))
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_trace(args):
     """Per-kernel summary of a rocprofv3 --kernel-trace --stats run of this workload: for every
     kernel of this library, launches, mean and median duration (end - start of each dispatch)
@@ -1079,6 +1140,9 @@ def main():
         return 0
     if args.summarize_mfma:
         summarize_mfma(args)
+        return 0
+    if args.summarize_sq:
+        summarize_sq(args)
         return 0
     if args.summarize_trace:
         summarize_trace(args)
