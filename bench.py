@@ -87,6 +87,9 @@ def parse():
                    help="skip the achievable-ceiling kernels (launch floor, plain reads, MFMA loop)")
     p.add_argument("--no-prefill", action="store_true",
                    help="2b_decode only: skip the prefill half of the metric (2B prefill GEMM at M = 2048)")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="2b_decode only: skip the other configurations (detail.workloads: 2B decode at 4 tokens, "
+                        "7B decode at 1, 4, 8, 2B prefill at 256, 100B decode at 1, 16)")
     p.add_argument("--cpu-cores", type=int, default=None,
                    help="worker processes of the all-cores oracle baseline (default: the usable cores, at most 16)")
     p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
@@ -113,7 +116,7 @@ def parse():
 # Token counts each workload is measured at (``--m``). tests/test_plan_coverage.py checks that
 # every kernel instance these steps launch -- default, --split and --row-scales routes -- is
 # also run by a parity test against the oracle.
-WORKLOAD_M = {"2b_decode": (1,), "7b_decode": (1, 2, 4, 8), "100b_decode": (1, 2, 4, 16), "2b_prefill": (256, 2048)}
+WORKLOAD_M = {"2b_decode": (1, 4), "7b_decode": (1, 2, 4, 8), "100b_decode": (1, 2, 4, 16), "2b_prefill": (256, 2048)}
 
 
 def step_plans(spec, split=False, row_scales=False, gemv_algo="auto"):
@@ -1117,6 +1120,34 @@ def prefill_detail(args, g, spec):
             "traced": traced_summary(spec, "k_gemm")}
 
 
+# The other configurations the default run measures besides the metric's two halves (2B decode
+# at one token, 2B prefill at 2048): each step timed as the main line's, reported compactly.
+EXTRA_WORKLOADS = [("2b_decode", 4), ("7b_decode", 1), ("7b_decode", 4), ("7b_decode", 8), ("2b_prefill", 256),
+                   ("100b_decode", 1), ("100b_decode", 16)]
+
+
+def workload_summary(args, name, M):
+    """One configuration's step: time, rate against its roofline (HBM for decode, int8 MFMA for
+    prefill), the per-launch interval of its product kernels and each shape's time in the step."""
+    spec = workload_spec(name, M)
+    if ROW_SCALES:
+        spec["desc"] += ", row-group weight scales (one per Q, K, V and gate, up block)"
+    g = run_gpu(args, spec)
+    prod_us = g["ms_prod"] * 1e3 / g["n_prod"]
+    out = {"workload": spec["desc"], "M": M, "layers": spec["layers"], "ms_per_step": round(g["ms_step"], 5),
+           "kernel": g["kernel"], "launch_interval_us": round(prod_us, 3),
+           "kernel_us_per_shape": {n: round(u, 3) for (n, _, _), u in zip(spec["shapes"], g["shape_us"])}}
+    if spec["prefill"]:
+        ach = g["step_ops"] / g["n_prod"] / (prod_us * 1e-6) / 1e12
+        out.update(step_TOPS=round(g["step_ops"] / (g["ms_step"] * 1e-3) / 1e12, 1), product_TOPS=round(ach, 1),
+                   frac_of_int8_peak=round(ach / INT8_PEAK_TOPS, 4))
+    else:
+        gbs = g["step_bytes"] / (g["ms_step"] * 1e-3) / 1e9
+        out.update(step_GBs=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+    g.pop("packed")
+    return out
+
+
 def traced_summary(spec, kernel):
     tr = traced_for(spec, kernel)
     if tr is None:
@@ -1195,6 +1226,10 @@ def main():
     elif spec["prefill"] and ceil is not None:
         roof["achievable"] = ceil["mfma_int8_TOPS"]
         roof["frac_of_achievable"] = round(ach / ceil["mfma_int8_TOPS"], 4)
+    workloads = None
+    if args.workload == "2b_decode" and M == 1 and not args.no_workloads and not args.split:
+        g.pop("packed", None)
+        workloads = [workload_summary(args, n, m) for n, m in EXTRA_WORKLOADS]
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, spec)
     detail = {"dominant_kernel": g["kernel"],
               "launch_interval_us": round(prod_us, 3),
@@ -1220,6 +1255,8 @@ def main():
             detail["step_frac_of_read_ceiling"] = ceil["step_frac_of_read_step"]
     if prefill is not None:
         detail["prefill"] = prefill
+    if workloads is not None:
+        detail["workloads"] = workloads
     line = {
         "metric": METRIC,
         "value": round(value, 2),

@@ -35,7 +35,7 @@ DEV = "cuda:0"
 # workload -> (seed config, layer shapes, token counts): the workloads bench.py times
 # (tests/test_plan_coverage.py checks every kernel instance they launch against these).
 ROUTE_WORKLOADS = {
-    "2b_decode": (synth.CFG_2B_DECODE, synth.SHAPES_2B, (1,)),
+    "2b_decode": (synth.CFG_2B_DECODE, synth.SHAPES_2B, (1, 4)),
     "7b_decode": (synth.CFG_7B_DECODE, synth.SHAPES_7B, (1, 2, 4, 8)),
     "100b_decode": (synth.CFG_100B_DECODE, synth.SHAPES_100B, (1, 2, 4, 16)),
     "2b_prefill": (synth.CFG_2B_PREFILL, synth.SHAPES_2B, (256, 2048)),
