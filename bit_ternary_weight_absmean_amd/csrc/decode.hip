@@ -136,6 +136,25 @@ __device__ inline void mfma_step_t(const v4i &w, const v4i (&b)[4], v4i &a1, v4i
 // 4 (d / 4)).
 __device__ inline int lds_x_offset(int k4) { return (k4 >> 4) * 64 + 16 * (k4 & 3) + 4 * ((k4 >> 2) & 3); }
 
+// The epilogue wave's sum of the other k-splits' partials: all NP LDS reads are issued before
+// the first add (one round trip; left to itself the compiler reuses the first reads'
+// registers for the later ones and waits in between). red: the first partner's slot, the
+// partners 64 slots apart.
+template <int NP>
+__device__ inline void add_ksplit_partials(const int4 *red, int (&part)[4])
+{
+    if constexpr (NP > 0) {
+        int4 o[NP];
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+            o[j] = red[j * 64];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+            part[0] += o[j].x, part[1] += o[j].y, part[2] += o[j].z, part[3] += o[j].w;
+    }
+}
+
 // Partial accumulators of all waves -> y and acc. red[w][k][v][lane]; o = m * rows + nl.
 // token_stats(m, qs, sx) supplies sum_k q and s_x of token m.
 // w_scale[rs ? n : 0] is the weight scale of output row n.
@@ -660,13 +679,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_linear_decode(
         if (ks != KE)
             red[wave * 64 + lane] = make_int4(part[0], part[1], part[2], part[3]);
         __syncthreads();
-        if (ks == KE) {
-#pragma unroll
-            for (int j = 0; j < KE; ++j) {
-                const int4 o = red[(wave - KE + j) * 64 + lane];
-                part[0] += o.x, part[1] += o.y, part[2] += o.z, part[3] += o.w;
-            }
-        }
+        if (ks == KE)
+            add_ksplit_partials<KE>(red + (wave - KE) * 64 + lane, part);
     }
     if (ks == KE && r < M) {
         int qs = 0;
@@ -827,13 +841,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv_staged(
         if (ks != KE)
             red[wave * 64 + lane] = make_int4(part[0], part[1], part[2], part[3]);
         __syncthreads();
-        if (ks == KE) {
-#pragma unroll
-            for (int j = 0; j < KE; ++j) {
-                const int4 o = red[(wave - KE + j) * 64 + lane];
-                part[0] += o.x, part[1] += o.y, part[2] += o.z, part[3] += o.w;
-            }
-        }
+        if (ks == KE)
+            add_ksplit_partials<KE>(red + (wave - KE) * 64 + lane, part);
     }
     if (ks == KE && r < M) {
         const float sc[4] = {gam.x * sx_r, gam.y * sx_r, gam.z * sx_r, gam.w * sx_r};
@@ -1023,13 +1032,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_gemv_blocked(
         if (ks != KE)
             red[wave * 64 + lane] = make_int4(part[0], part[1], part[2], part[3]);
         __syncthreads();
-        if (ks == KE) {
-#pragma unroll
-            for (int j = 0; j < KE; ++j) {
-                const int4 o = red[(wave - KE + j) * 64 + lane];
-                part[0] += o.x, part[1] += o.y, part[2] += o.z, part[3] += o.w;
-            }
-        }
+        if (ks == KE)
+            add_ksplit_partials<KE>(red + (wave - KE) * 64 + lane, part);
     }
     if (ks == KE && r < M) {
         const float sc[4] = {gam.x * sx_r, gam.y * sx_r, gam.z * sx_r, gam.w * sx_r};
