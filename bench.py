@@ -92,7 +92,7 @@ def parse():
                         "7B decode at 1, 4, 8, 2B prefill at 256, 100B decode at 1, 16)")
     p.add_argument("--cpu-cores", type=int, default=None,
                    help="worker processes of the all-cores oracle baseline (default: the usable cores, at most 16)")
-    p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
+    p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR[,TRACE_DIR...]", "OUT_MD"),
                    help="write a per-kernel summary (durations and launch intervals) of a rocprofv3 --kernel-trace "
                         "--stats run of this workload")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
@@ -951,30 +951,45 @@ def summarize_trace(args):
     more than the graph's time."""
     import statistics
 
-    trace_dir, out_md = args.summarize_trace
-    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
-    rows = []
-    for f in files:
-        with open(f) as fh:
-            rows += list(csv.DictReader(fh))
-    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    # TRACE_DIR may list several runs of the same command, comma-separated: the tables cover
+    # them all, and the dominant kernel's figure is the median of the runs' means (the tracer's
+    # spacing of dispatches, and so a short kernel's traced duration, varies from run to run)
+    trace_dirs, out_md = args.summarize_trace[0].split(","), args.summarize_trace[1]
+
+    def load(trace_dir):
+        files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+        rows = []
+        for f in files:
+            with open(f) as fh:
+                rows += list(csv.DictReader(fh))
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        per = collections.OrderedDict()
+        for i, r in enumerate(rows):
+            name = r["Kernel_Name"]
+            if not any(k in name for k in ("k_linear_decode", "k_gemv", "k_gemm", "k_quant_act", "k_read", "k_empty",
+                                           "k_store_one", "k_mfma_loop", "k_pack", "k_gamma", "k_row_abs_sum")):
+                continue
+            start, end = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            key = (name, r.get("Grid_Size", r.get("Grid_Size_X", "")),
+                   r.get("Workgroup_Size", r.get("Workgroup_Size_X", "")))
+            e = per.setdefault(key, {"dur": [], "gap": []})
+            e["dur"].append((end - start) / 1e3)
+            if i + 1 < len(rows):
+                nxt = int(rows[i + 1]["Start_Timestamp"])
+                if 0 <= nxt - start <= 50_000:
+                    e["gap"].append((nxt - start) / 1e3)
+        return per
+
+    runs = [load(d) for d in trace_dirs]
     per = collections.OrderedDict()
-    for i, r in enumerate(rows):
-        name = r["Kernel_Name"]
-        if not any(k in name for k in ("k_linear_decode", "k_gemv", "k_gemm", "k_quant_act", "k_read", "k_empty",
-                                       "k_store_one", "k_mfma_loop", "k_pack", "k_gamma", "k_row_abs_sum")):
-            continue
-        start, end = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
-        key = (name, r.get("Grid_Size", r.get("Grid_Size_X", "")),
-               r.get("Workgroup_Size", r.get("Workgroup_Size_X", "")))
-        e = per.setdefault(key, {"dur": [], "gap": []})
-        e["dur"].append((end - start) / 1e3)
-        if i + 1 < len(rows):
-            nxt = int(rows[i + 1]["Start_Timestamp"])
-            if 0 <= nxt - start <= 50_000:
-                e["gap"].append((nxt - start) / 1e3)
+    for pr in runs:
+        for key, e in pr.items():
+            m = per.setdefault(key, {"dur": [], "gap": []})
+            m["dur"] += e["dur"]
+            m["gap"] += e["gap"]
+    trace_dir = trace_dirs[0]
     lines = [f"# Kernel trace: {args.workload} workload" + (f" (M={args.m})" if args.m else ""), "",
              "Command (run from the repository root):", "", f"    {args.command}", "",
              "Per kernel instance and launch shape: dispatch durations (end - start) and the interval from a",
@@ -1025,15 +1040,19 @@ def summarize_trace(args):
         alg = [linear_bytes(M, N, K) if kname == "k_linear_decode" else gemv_bytes(M, N, K)
                for _, N, K in spec["shapes"]]
         ops = [2 * M * N * K for _, N, K in spec["shapes"]]
+        run_means = [statistics.mean([x for (n, _, _), e in pr.items() if is_kernel(n, kname) for x in e["dur"]])
+                     for pr in runs]
         rec = {"kernel": kname, "workload": spec["desc"], "M": M, "source_sha256": source_hash(kname),
-               "dispatches": len(d), "mean_duration_us": round(statistics.mean(d), 3),
+               "dispatches": len(d), "mean_duration_us": round(statistics.median(run_means), 3),
+               "run_mean_duration_us": [round(x, 3) for x in run_means],
                "mean_interval_us": round(statistics.mean(gp), 3) if gp else None,
                "algorithmic_bytes_per_launch": round(sum(alg) / len(alg)),
                "ops_per_launch": round(sum(ops) / len(ops)), "command": args.command}
         with open(os.path.splitext(out_md)[0] + ".json", "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")
-        lines += ["", f"Dominant kernel of the workload: `{kname}`, {len(d)} dispatches, mean duration "
+        lines += ["", f"Dominant kernel of the workload: `{kname}`, {len(d)} dispatches over {len(runs)} run(s), mean "
+                      f"duration per run {', '.join(f'{x:.3f}' for x in run_means)} us, median "
                       f"{rec['mean_duration_us']} us; algorithmic bytes per launch {rec['algorithmic_bytes_per_launch']} "
                       f"-> {rec['algorithmic_bytes_per_launch'] / rec['mean_duration_us'] / 1e3:.1f} GB/s, "
                       f"{rec['ops_per_launch'] / rec['mean_duration_us'] / 1e6:.1f} TOP/s at the traced mean.",
@@ -1044,7 +1063,7 @@ def summarize_trace(args):
                   "microseconds apart (see the interval columns; the empty kernel shows the same spacing), so each",
                   "dispatch above ran alone from a cold start, and its mean duration is the conservative figure the",
                   "line reports as `detail.traced` (read from the JSON next to this file while the kernel's",
-                  "sources are unchanged)."]
+                  "sources are unchanged; with several runs, the median of their means)."]
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))

@@ -151,3 +151,29 @@ def test_source_hash_ignores_comments_and_blank_lines(tmp_path, monkeypatch):
 def test_kernel_sources_exist(kernel):
     for f in bench.KERNEL_SOURCES[kernel]:
         assert os.path.exists(os.path.join(bench.CSRC, f)), f
+
+
+def test_summarize_trace_takes_the_median_of_runs(tmp_path):
+    """Several trace runs of one command: the dominant kernel's figure is the median of the runs' means."""
+    dec = "void bt::(anonymous namespace)::k_linear_decode<1, 8, 2, 1, false>(...)"
+    fields = ["Kernel_Name", "Grid_Size", "Workgroup_Size", "Start_Timestamp", "End_Timestamp"]
+    dirs = []
+    for run, dur_ns in enumerate((3000, 5000, 4000)):
+        d = tmp_path / f"tr{run}"
+        d.mkdir()
+        with open(d / "run_kernel_trace.csv", "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=fields)
+            w.writeheader()
+            for i in range(10):  # dispatches 8 us apart
+                t0 = 1_000_000 * run + 8000 * i
+                w.writerow({"Kernel_Name": dec, "Grid_Size": 122880, "Workgroup_Size": 512, "Start_Timestamp": t0,
+                            "End_Timestamp": t0 + dur_ns})
+        dirs.append(str(d))
+    out = tmp_path / "trace.md"
+    r = run_bench("--summarize-trace", ",".join(dirs), str(out), "--command", "synthetic")
+    assert r.returncode == 0, r.stderr
+    rec = json.loads((tmp_path / "trace.json").read_text())
+    assert rec["run_mean_duration_us"] == [3.0, 5.0, 4.0]
+    assert rec["mean_duration_us"] == 4.0
+    assert rec["dispatches"] == 30
+    assert rec["mean_interval_us"] == 8.0
