@@ -705,6 +705,47 @@ __global__ __launch_bounds__(kKsWaves * 64) void k_gemm_ks(
             d[i] += *reinterpret_cast<const v4i *>(area(wave) + ((s * 4 + i) * 64 + lane) * 16);
 
     // Epilogue of token tile `wave`: lane (g, r) holds tokens 16 wave + 4 g + v, row 16 i + r.
+    const bool vec = (N & 3) == 0 && ((reinterpret_cast<uintptr_t>(Y) | reinterpret_cast<uintptr_t>(ACC)) & 15) == 0;
+    if (vec) {
+        // Row-contiguous 16-byte stores (16 lanes per 256-byte row piece) instead of 4-byte
+        // fragments: each output passes through a slab of 16 tokens x 64 rows (pitch 68
+        // words: the MFMA-layout writes and the 16-byte row reads hit distinct banks) in the
+        // wave's own exchange area, whose partials it has read. The compiler barriers keep the
+        // slab's write / read / next write order; LDS performs a wave's accesses in that order.
+        constexpr int kPitchW = 68;
+        int32_t *slab = reinterpret_cast<int32_t *>(area(wave));
+        const int rq = lane & 15, rrow = lane >> 4;  // read: 4-row quad rq, slab row 4 p + rrow
+        auto through = [&](auto value, auto store) {
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    slab[(4 * g + v) * kPitchW + 16 * i + r] = value(i, v);
+            asm volatile("" ::: "memory");
+            v4i rows4[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                rows4[p] = *reinterpret_cast<const v4i *>(slab + (4 * p + rrow) * kPitchW + 4 * rq);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int64_t m = m0 + 16 * wave + 4 * p + rrow, n = n0 + 4 * rq;
+                if (m < M && n < N)
+                    store(m * N + n, rows4[p]);
+            }
+        };
+        if (ACC)
+            through([&](int i, int v) { return d[i][v] - xs_v[v]; },
+                    [&](int64_t o, v4i x) { __builtin_nontemporal_store(x, reinterpret_cast<v4i *>(ACC + o)); });
+        if (Y)
+            through([&](int i, int v) { return __float_as_int((float)(d[i][v] - xs_v[v]) * (gam_i[i] * sx_v[v])); },
+                    [&](int64_t o, v4i x) {
+                        const v4f y = {__int_as_float(x[0]), __int_as_float(x[1]), __int_as_float(x[2]),
+                                       __int_as_float(x[3])};
+                        __builtin_nontemporal_store(y, reinterpret_cast<v4f *>(Y + o));
+                    });
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t n = n0 + 16 * i + r;
