@@ -164,10 +164,13 @@ def test_gemv_small(M, N, K, algo):
 # (257, 516, 700), and its k-share edges: 4 steps (one per wave), 5 steps of 9 chunks
 # (shares 2, 2, 1, 0), 5 whole steps, exactly 256 tiles (3-stage ring, one workgroup per CU)
 # and 257 to 512 tiles (2-stage ring, two per CU; ragged, and exactly 512); and the longest
-# rows (K = 28672: 112 steps, 28 per wave).
+# rows (K = 28672: 112 steps, 28 per wave). The small-M form stores 16-byte row pieces where
+# N % 4 == 0 and 4-byte fragments otherwise: (100, 130, 640) and (257, 515, 700) take the
+# latter on the 3-stage ring, (300, 3501, 900) on the 2-stage one (275 tiles).
 GEMM_SMALL = [(1, 64, 64), (17, 100, 300), (128, 512, 256), (129, 130, 129), (300, 200, 517), (64, 1000, 2560),
               (257, 516, 700), (1024, 8448, 512), (64, 64, 512), (200, 700, 513), (100, 130, 640),
-              (256, 4096, 1024), (300, 3500, 900), (512, 4096, 768), (40, 1000, 28672)]
+              (256, 4096, 1024), (300, 3500, 900), (512, 4096, 768), (40, 1000, 28672), (257, 515, 700),
+              (300, 3501, 900)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SMALL)
@@ -177,6 +180,31 @@ def test_gemm_small(M, N, K):
     X = synth.gaussian((M, K), 9600 + M)
     ref = oracle_layer(W, X)
     check_product(gpu_pack(W), gpu_quant(X), ref, M, N, bt.ternary_gemm)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 517), (300, 3500, 900), (1024, 8448, 512)])
+@pytest.mark.parametrize("shift_y,shift_acc", [(1, 0), (0, 3), (2, 2)])
+def test_gemm_outputs_not_16_byte_aligned(M, N, K, shift_y, shift_acc):
+    """Caller outputs that start 4, 8 or 12 bytes past a 16-byte boundary (views into larger
+    buffers): both GEMM forms fall back to element stores there; the results match the oracle
+    and no element outside the views is written."""
+    note(f"gemm unaligned outputs M={M} N={N} K={K} shifts {shift_y} {shift_acc}")
+    W = synth.gaussian((N, K), 9100 + N, 0.02)
+    X = synth.gaussian((M, K), 9600 + M)
+    ref = oracle_layer(W, X)
+    ybuf = torch.full((M * N + 8,), 1234.5, dtype=torch.float32, device=DEV)
+    abuf = torch.full((M * N + 8,), -7, dtype=torch.int32, device=DEV)
+    Yv = ybuf[shift_y:shift_y + M * N].view(M, N)
+    Av = abuf[shift_acc:shift_acc + M * N].view(M, N)
+    assert (Yv.data_ptr() % 16 != 0) or (Av.data_ptr() % 16 != 0)
+    bt.ternary_gemm(gpu_pack(W), gpu_quant(X), out_y=Yv, out_acc=Av)
+    torch.cuda.synchronize()
+    bad = np.argwhere(Av.cpu().numpy() != ref["acc"])
+    assert bad.size == 0, f"{len(bad)} acc mismatches, first at {bad[:5].tolist()}"
+    assert tol_ok(Yv.cpu().numpy(), ref["Y"])
+    yb, ab = ybuf.cpu().numpy(), abuf.cpu().numpy()
+    assert (yb[:shift_y] == 1234.5).all() and (yb[shift_y + M * N:] == 1234.5).all()
+    assert (ab[:shift_acc] == -7).all() and (ab[shift_acc + M * N:] == -7).all()
 
 
 def test_tiny_workload_all_paths():
