@@ -539,6 +539,31 @@ def test_linear_fused(M, N, K):
     np.testing.assert_array_equal(Y.cpu().numpy(), Ys.cpu().numpy())
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 3840, 2560), (4, 300, 1000), (8, 2560, 6912), (16, 1000, 2560)])
+@pytest.mark.parametrize("shift_y,shift_acc", [(1, 0), (0, 3), (2, 2)])
+def test_linear_outputs_not_16_byte_aligned(M, N, K, shift_y, shift_acc):
+    """Caller outputs that start 4, 8 or 12 bytes past a 16-byte boundary (views into larger
+    buffers) on the decode routes (fused at 1 and 4 tokens, quantizer + staged product at 8
+    and 16): their four-output stores fall back to element stores; the results match the
+    oracle and no element outside the views is written."""
+    note(f"linear unaligned outputs M={M} N={N} K={K} shifts {shift_y} {shift_acc}")
+    W = synth.gaussian((N, K), 9400 + N + K, 0.02)
+    X = synth.gaussian((M, K), 9900 + M + K)
+    ref = oracle_layer(W, X)
+    ybuf = torch.full((M * N + 8,), 1234.5, dtype=torch.float32, device=DEV)
+    abuf = torch.full((M * N + 8,), -7, dtype=torch.int32, device=DEV)
+    Yv = ybuf[shift_y:shift_y + M * N].view(M, N)
+    Av = abuf[shift_acc:shift_acc + M * N].view(M, N)
+    bt.linear(to_dev(X), gpu_pack(W), out_y=Yv, out_acc=Av)
+    torch.cuda.synchronize()
+    bad = np.argwhere(Av.cpu().numpy() != ref["acc"])
+    assert bad.size == 0, f"{len(bad)} acc mismatches, first at {bad[:5].tolist()}"
+    assert tol_ok(Yv.cpu().numpy(), ref["Y"])
+    yb, ab = ybuf.cpu().numpy(), abuf.cpu().numpy()
+    assert (yb[:shift_y] == 1234.5).all() and (yb[shift_y + M * N:] == 1234.5).all()
+    assert (ab[:shift_acc] == -7).all() and (ab[shift_acc + M * N:] == -7).all()
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 3840, 2560), (4, 300, 1000), (2, 600, 6912), (8, 500, 2560)])
 def test_linear_misaligned_input(M, N, K):
     """Token rows at a 4-byte (not 16-byte) offset with K % 4 == 0: the fused kernel then reads
